@@ -1,0 +1,483 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises ``AssertionError`` when
+the oracle disagrees with a worked example, a closed form, an invariant, a brute-force
+search, or a library routine.  ``test_oracle_pins.py`` runs them against the oracle;
+``test_oracle_mutants.py`` runs them against deliberately broken copies of the
+oracle to show that each plausible mistake is caught by at least one pin.
+
+Method source throughout: "Accelerating Parallel Diffusion Model Serving with
+Residual Compression" (CompactFusion summary): section Approach (residual against the
+previous reconstruction, sender-side error feedback, low rank + INT4), the
+measured-effects table (Compact-1bit / Compact-2bit, warmup, rank 32 with INT4,
+2 vs 10 iterations), Surprising findings (naive 1-bit collapses; residual + EF stays
+close), and Experimental setup "Builds on" (error feedback from gradient compression,
+PowerSGD-style subspace iteration).
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+import sys
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+import gen  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers ----
+def load_golden(name: str) -> dict:
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, val = line.split(":", 1)
+            out[key.strip()] = val.split()
+    return out
+
+
+def unpack_codes(codes: np.ndarray, bits: int, numel: int) -> np.ndarray:
+    """Independent numpy unpack: LSB-first, `bits` per element."""
+    if bits == 1:
+        return np.unpackbits(codes, bitorder="little")[:numel].astype(np.uint8)
+    c = codes.astype(np.uint8)
+    return np.stack([(c >> s) & 3 for s in (0, 2, 4, 6)], axis=1).reshape(-1)[:numel]
+
+
+def decode_numpy(codes, scales, bits, numel) -> np.ndarray:
+    """fp32 decoded values from codes/scales, written from the level definitions."""
+    c = unpack_codes(codes, bits, numel)
+    s = np.repeat(scales.astype(np.float32), 128)[:numel]
+    if bits == 1:
+        return np.where(c == 1, -s, s).astype(np.float32)
+    lvl = np.where((c & 2) != 0, np.float32(1.5) * s, np.float32(0.5) * s).astype(np.float32)
+    return np.where((c & 1) != 0, -lvl, lvl).astype(np.float32)
+
+
+def tiny_trajectory(steps: int, seed: int = 0):
+    wl = dataclasses.replace(gen.WORKLOADS["tiny"], steps=steps)
+    tr = gen.Trajectory(wl, seed)
+    return [tr.next()[0].copy() for _ in range(steps)]
+
+
+def scaled_trajectory(m: int, n: int, steps: int, seed: int = 0):
+    """FLUX-like distribution (channel scales + outliers) at a small shape, bf16."""
+    wl = gen.Workload("small", m, n, 1, steps, "bf16", True)
+    tr = gen.Trajectory(wl, seed)
+    return [tr.next()[0].copy() for _ in range(steps)]
+
+
+def f32(x):
+    return gen.as_f32(x).astype(np.float32)
+
+
+# ------------------------------------------------------------ worked examples
+def _golden_group(O, name):
+    g = load_golden(name)
+    bits = int(g["bits"][0])
+    a = np.zeros(128, np.float32)
+    r = np.array([float(v) for v in g["r"]], np.float32)
+    a[: r.size] = r
+    ahat = np.zeros(128, np.float32)
+    err = np.zeros(128, np.float32)
+    codes, scales = O.compress(bits, a, ahat, err)
+    assert scales[0] == np.float32(float(g["scale"][0])), (scales[0], g["scale"])
+    want = bytes(int(h, 16) for h in g["codes_hex"])
+    assert codes.tobytes() == want, (codes.tobytes().hex(), want.hex())
+    d = np.full(128, np.float32(float(g["d_rest"][0])), np.float32)
+    dl = np.array([float(v) for v in g["d"]], np.float32)
+    d[: dl.size] = dl
+    assert np.array_equal(ahat, d), (ahat[:8], d[:8])
+    rx = np.zeros(128, np.float32)
+    O.decompress(bits, codes, scales, rx)
+    assert np.array_equal(rx, d)
+
+
+def pin_golden_q1(O):
+    _golden_group(O, "q1_group.txt")
+
+
+def pin_golden_q2(O):
+    _golden_group(O, "q2_group.txt")
+
+
+def pin_golden_int4(O):
+    g = load_golden("int4_factor.txt")
+    rows, k = int(g["rows"][0]), int(g["k"][0])
+    x = np.array([float(v) for v in g["x"]], np.float32).reshape(rows, k)
+    packed, scales = O.int4_quantize(x)
+    assert packed.tobytes() == bytes(int(h, 16) for h in g["packed_hex"]), packed.tobytes().hex()
+    assert np.array_equal(scales, np.array([float(v) for v in g["scales"]], np.float32))
+    xh = O.int4_dequantize(packed, scales, rows, k)
+    assert np.array_equal(xh.reshape(-1), np.array([float(v) for v in g["xhat"]], np.float32))
+
+
+# -------------------------------------------------------------- special cases
+def pin_init(O):
+    traj = scaled_trajectory(16, 256, 1)
+    a = traj[0]
+    ahat = np.full(a.shape, 7.0, np.float32)
+    err = np.full(a.shape, 7.0, np.float32)
+    O.init_state(a, ahat, err)
+    assert np.array_equal(ahat, f32(a)) and not err.any()
+    t = tiny_trajectory(1)[0]
+    ah = np.zeros_like(t)
+    O.init_state(t, ah, None)
+    assert np.array_equal(ah, t)
+
+
+def pin_zero_residual(O):
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((8, 256)).astype(np.float32)
+    for bits in (1, 2):
+        ahat = a.copy()
+        err = np.full_like(a, 5.0)
+        codes, scales = O.compress(bits, a, ahat, err)
+        assert not codes.any() and not scales.any()
+        assert np.array_equal(ahat, a) and not err.any()
+    ahat = a.copy()
+    err = np.full_like(a, 5.0)
+    q = rng.standard_normal((256, 4)).astype(np.float32)
+    q0 = q.copy()
+    u, us, v, vs = O.lowrank_compress(a, ahat, err, q, 4, 2, 4)
+    assert not u.any() and not v.any() and not us.any() and not vs.any()
+    assert np.array_equal(ahat, a) and not err.any()
+    assert np.array_equal(q, q0), "guard-zeroed columns keep their start vector"
+
+
+# ------------------------------------------------------------------ invariants
+def pin_ef_invariant(O):
+    """e_t = fl(a_t - Ahat_t) bitwise; e_t is within 2 ulp of the textbook fl(r - d);
+    the explicit form (r = dA + e_prev, e = r - d) gives the same trajectory up to
+    fp32 rounding."""
+    for bits in (1, 2):
+        traj = tiny_trajectory(6)
+        a0 = traj[0]
+        ahat = np.empty_like(a0)
+        err = np.empty_like(a0)
+        O.init_state(a0, ahat, err)
+        ahat_x, err_x = ahat.copy(), err.copy()
+        for t in range(1, len(traj)):
+            a = traj[t]
+            prev = ahat.copy()
+            r = (a - ahat).astype(np.float32)
+            codes, scales = O.compress(bits, a, ahat, err)
+            d = decode_numpy(codes, scales, bits, a.size).reshape(a.shape)
+            assert np.array_equal(err, (a - ahat).astype(np.float32))
+            textbook = (r - d).astype(np.float32)
+            # three roundings separate the two forms; bound them by the largest operand
+            mag = np.maximum.reduce([np.abs(a), np.abs(prev), np.abs(ahat), np.abs(d)])
+            assert np.all(np.abs(err - textbook) <= 2 * np.spacing(mag))
+            O.compress_explicit_ef(bits, a, traj[t - 1], ahat_x, err_x)
+            scale = np.abs(ahat).max()
+            far = np.abs(ahat_x - ahat) > 1e-5 * scale
+            assert far.mean() <= 1e-3, far.mean()
+            assert np.abs(err_x - err).max() <= 1e-5 * scale or far.any()
+
+
+def pin_ef_bounded(O):
+    """Error feedback keeps ||A_t - Ahat_t|| bounded; without it the error grows
+    (measured-effects table, EF ablation; Surprising findings)."""
+    traj = tiny_trajectory(28)
+    a0 = traj[0]
+    ahat = np.empty_like(a0)
+    err = np.empty_like(a0)
+    O.init_state(a0, ahat, err)
+    ahat_n = a0.copy()
+    ratios, ratios_n = [], []
+    for t in range(1, len(traj)):
+        a = traj[t]
+        step = np.linalg.norm(a - traj[t - 1])
+        O.compress(1, a, ahat, err)
+        O.compress_noef(1, a, traj[t - 1], ahat_n)
+        ratios.append(np.linalg.norm(a - ahat) / step)
+        ratios_n.append(np.linalg.norm(a - ahat_n) / step)
+        assert np.linalg.norm(err) == np.linalg.norm((a - ahat).astype(np.float32))
+    assert abs(ratios[0] - np.sqrt(1 - 2 / np.pi)) < 0.02  # first step: plain 1-bit of N(0,s^2)
+    assert max(ratios) < 0.85, ratios
+    assert ratios_n[-1] > 2.5 and ratios_n[-1] > 3 * ratios[-1], (ratios_n[-1], ratios[-1])
+
+
+def pin_q1_least_squares(O):
+    """For sign codes the least-squares group scale is mean|r|, and then
+    sum (r-d)^2 = sum r^2 - (sum|r|)^2 / 128 per group; for Gaussian r the
+    relative error is sqrt(1 - 2/pi)."""
+    rng = np.random.default_rng(2)
+    n = 128 * 2048
+    r = (rng.standard_normal(n) * np.repeat(rng.lognormal(0, 1, n // 128), 128)).astype(np.float32)
+    ahat = np.zeros(n, np.float32)
+    err = np.zeros(n, np.float32)
+    codes, scales = O.compress(1, r, ahat, err)
+    d = decode_numpy(codes, scales, 1, n).astype(np.float64)
+    rg = r.astype(np.float64).reshape(-1, 128)
+    lhs = ((rg - d.reshape(-1, 128)) ** 2).sum(1)
+    rhs = (rg ** 2).sum(1) - np.abs(rg).sum(1) ** 2 / 128
+    assert np.allclose(lhs, rhs, rtol=1e-5, atol=1e-6 * (rg ** 2).sum(1).max())
+    s64 = np.abs(rg).mean(1)
+    assert np.all(np.abs(scales - s64) <= 64 * np.spacing(scales))
+    g = rng.standard_normal(n).astype(np.float32)
+    ah = np.zeros(n, np.float32)
+    e2 = np.zeros(n, np.float32)
+    O.compress(1, g, ah, e2)
+    ratio = np.linalg.norm(e2) / np.linalg.norm(g)
+    assert abs(ratio - np.sqrt(1 - 2 / np.pi)) < 0.01, ratio
+
+
+def _nearest_level_codes(r, s):
+    """Brute force over the 4 levels, in fp64 with exact levels; ties go to the
+    inner level, and r = 0 to +0.5 s."""
+    r = r.astype(np.float64)
+    s = s.astype(np.float64)
+    levels = np.array([0.5, -0.5, 1.5, -1.5])  # codes 0, 1, 2, 3 (sign | mag << 1)
+    dist = np.abs(r[:, None] - levels[None, :] * s[:, None])
+    best = np.argmin(dist, axis=1)  # argmin keeps the first: inner levels, +0.5 first
+    return best.astype(np.uint8)
+
+
+def pin_q2_bruteforce(O):
+    rng = np.random.default_rng(3)
+    n = 128 * 1024
+    r = (rng.standard_normal(n) * np.repeat(rng.lognormal(0, 1, n // 128), 128)).astype(np.float32)
+    # exact ties at |r| = s and zeros in a few groups
+    r[:128] = 0
+    r[128:131] = [3.0, 2.0, -2.0]
+    r[131:256] = 0.5
+    r[256:384] = -0.0
+    ahat = np.zeros(n, np.float32)
+    err = np.zeros(n, np.float32)
+    codes, scales = O.compress(2, r, ahat, err)
+    assert np.array_equal(scales, (np.abs(r).reshape(-1, 128).max(1) / np.float32(1.5)).astype(np.float32))
+    got = unpack_codes(codes, 2, n)
+    want = _nearest_level_codes(r, np.repeat(scales, 128))
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:10]
+    d = decode_numpy(codes, scales, 2, n)
+    s = np.repeat(scales, 128).astype(np.float64)
+    assert np.all(np.abs(r.astype(np.float64) - d) <= 0.5 * s * (1 + 1e-6))
+    assert np.all(np.abs(r) <= (np.float32(1.5) * np.repeat(scales, 128)) * (1 + 2.0 ** -22))
+
+
+def pin_scaling(O):
+    """Scaling a and Ahat by 2^j leaves codes unchanged and scales every float by 2^j."""
+    traj = tiny_trajectory(3)
+    for bits in (1, 2):
+        for j in (5, -7):
+            f = np.float32(2.0 ** j)
+            a0 = traj[0]
+            ah, er = np.empty_like(a0), np.empty_like(a0)
+            O.init_state(a0, ah, er)
+            ahs, ers = ah * f, er * f
+            for t in (1, 2):
+                c1, s1 = O.compress(bits, traj[t], ah, er)
+                c2, s2 = O.compress(bits, (traj[t] * f).astype(np.float32), ahs, ers)
+                assert np.array_equal(c1, c2)
+                assert np.array_equal(s1 * f, s2) and np.array_equal(ah * f, ahs)
+                assert np.array_equal(er * f, ers)
+
+
+def pin_negation(O):
+    """Negating a and Ahat flips sign codes where r != 0 and keeps magnitudes and scales."""
+    traj = tiny_trajectory(2)
+    for bits in (1, 2):
+        a0, a1 = traj
+        ah = np.empty_like(a0)
+        er = np.empty_like(a0)
+        O.init_state(a0, ah, er)
+        ah = (ah + np.float32(0.01) * np.sign(a0)).astype(np.float32)  # non-trivial Ahat
+        ahn = -ah
+        ern = np.empty_like(er)
+        r = (a1 - ah).astype(np.float32)
+        c1, s1 = O.compress(bits, a1, ah, er)
+        c2, s2 = O.compress(bits, -a1, ahn, ern)
+        assert np.array_equal(s1, s2)
+        u1, u2 = unpack_codes(c1, bits, r.size), unpack_codes(c2, bits, r.size)
+        nz = r.reshape(-1) != 0
+        assert np.array_equal((u1 ^ u2)[nz], np.ones(nz.sum(), np.uint8))
+        assert not (u1 ^ u2)[~nz].any()
+        assert np.array_equal(ahn, -ah) and np.array_equal(ern, -er)
+
+
+def pin_sender_receiver(O):
+    """The receiver's reconstruction equals the sender's bit for bit every step."""
+    for bits in (1, 2):
+        traj = scaled_trajectory(32, 384, 5)
+        a0 = traj[0]
+        ah = np.empty(a0.shape, np.float32)
+        er = np.empty_like(ah)
+        O.init_state(a0, ah, er)
+        rx = np.empty_like(ah)
+        O.init_state(a0, rx)
+        for t in range(1, len(traj)):
+            prev = rx.copy()
+            codes, scales = O.compress(bits, traj[t], ah, er)
+            O.decompress(bits, codes, scales, rx)
+            assert np.array_equal(rx, ah)
+            d = decode_numpy(codes, scales, bits, ah.size).reshape(ah.shape)
+            assert np.array_equal(rx, (prev + d).astype(np.float32))
+
+
+def pin_2bit_beats_1bit(O):
+    """2-bit tracks the trajectory more closely than 1-bit (measured-effects table),
+    and naive 1-bit of the full activation collapses (Surprising findings)."""
+    for traj, ratio in ((tiny_trajectory(28), 0.9), (scaled_trajectory(64, 512, 28), 0.8)):
+        errs = {}
+        for bits in (1, 2):
+            ah = np.empty(traj[0].shape, np.float32)
+            er = np.empty_like(ah)
+            O.init_state(traj[0], ah, er)
+            for t in range(1, len(traj)):
+                O.compress(bits, traj[t], ah, er)
+            errs[bits] = np.linalg.norm(er)
+        assert errs[2] < ratio * errs[1], errs
+        # naive 1-bit of the activation itself: error ~0.6 |A| against ~|dA| with EF
+        out, _, _ = O.quantize_naive(1, traj[-1])
+        naive = np.linalg.norm(f32(traj[-1]) - out)
+        assert naive > 4 * errs[1], (naive, errs[1])
+
+
+# -------------------------------------------------------------------- low rank
+def pin_lowrank_full_rank(O):
+    """At k = min(m, n) with fp32 factors the residual is reproduced (<= 1e-5)."""
+    rng = np.random.default_rng(4)
+    for m, n in ((64, 32), (40, 96)):
+        k = min(m, n)
+        a = rng.standard_normal((m, n)).astype(np.float32)
+        ahat = (0.5 * rng.standard_normal((m, n))).astype(np.float32)
+        r = (a - ahat).astype(np.float64)
+        err = np.zeros_like(a)
+        q = rng.standard_normal((n, k)).astype(np.float32)
+        u, us, v, vs = O.lowrank_compress(a, ahat, err, q, k, 1, 32)
+        rhat = u.astype(np.float64) @ v.astype(np.float64).T
+        assert np.linalg.norm(rhat - r) / np.linalg.norm(r) <= 1e-5
+        assert np.linalg.norm(err) / np.linalg.norm(r) <= 1e-5
+        ptp = u.astype(np.float64).T @ u.astype(np.float64)
+        assert np.abs(ptp - np.eye(k)).max() < 1e-5, "U is orthonormal"
+
+
+def pin_lowrank_planted(O):
+    """A residual of rank k0 <= k is reproduced after one iteration."""
+    rng = np.random.default_rng(5)
+    m, n, k0, k = 96, 160, 3, 8
+    # small integer factors: the product is exact in fp32, so r has rank exactly k0
+    r = (rng.integers(-3, 4, (m, k0)) @ rng.integers(-3, 4, (k0, n))).astype(np.float32)
+    a = r.copy()
+    ahat = np.zeros_like(a)
+    err = np.zeros_like(a)
+    q = rng.standard_normal((n, k)).astype(np.float32)
+    u, us, v, vs = O.lowrank_compress(a, ahat, err, q, k, 1, 32)
+    assert np.linalg.norm(ahat - r) / np.linalg.norm(r) <= 1e-5
+    assert np.count_nonzero(np.abs(u).sum(0)) == k0, "rank-deficient columns are zeroed"
+
+
+def pin_lowrank_eckart_young(O):
+    """Subspace iteration converges to the best rank-k error sqrt(sum_{i>k} s_i^2)
+    (from LAPACK's SVD) and never goes below it."""
+    rng = np.random.default_rng(6)
+    m, n, k = 48, 40, 4
+    U, _ = np.linalg.qr(rng.standard_normal((m, n)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    sig = 0.7 ** np.arange(n)
+    r = ((U * sig) @ V.T).astype(np.float32)
+    s = np.linalg.svd(r.astype(np.float64), compute_uv=False)
+    best = np.sqrt((s[k:] ** 2).sum())
+    res = []
+    for iters in (1, 40):
+        a = r.copy()
+        ahat = np.zeros_like(a)
+        err = np.zeros_like(a)
+        q = rng.standard_normal((n, k)).astype(np.float32)
+        O.lowrank_compress(a, ahat, err, q, k, iters, 32)
+        e = np.linalg.norm(r.astype(np.float64) - ahat)
+        assert e >= best * (1 - 1e-5)
+        res.append(e)
+    assert res[1] <= best * (1 + 1e-4), (res, best)
+    assert res[0] > res[1]
+
+
+def pin_int4_bruteforce(O):
+    rng = np.random.default_rng(7)
+    rows, k = 300, 8
+    x = (rng.standard_normal((rows, k)) * rng.lognormal(0, 1, k)).astype(np.float32)
+    x[5, 3] = 0.0
+    x[:, 6] = 0.0  # zero column -> scale 0, codes 0
+    packed, scales = O.int4_quantize(x)
+    want_s = (np.abs(x).max(0) / np.float32(7)).astype(np.float32)
+    assert np.array_equal(scales, want_s)
+    b = packed.reshape(rows, k // 2)
+    nib = np.stack([b & 0xF, b >> 4], axis=2).reshape(rows, k).astype(np.int16)
+    c = np.where(nib >= 8, nib - 16, nib)
+    for j in range(k):
+        if scales[j] == 0:
+            assert not c[:, j].any()
+            continue
+        cand = np.arange(-7, 8)
+        q = (x[:, j] / scales[j]).astype(np.float32).astype(np.float64)  # the fp32 quotient
+        dist = np.abs(q[:, None] - cand[None, :])
+        dmin = dist.min(1, keepdims=True)
+        ties = dist == dmin
+        even = ties & (cand[None, :] % 2 == 0)
+        pick = np.where(ties.sum(1) > 1, cand[np.argmax(even, 1)], cand[np.argmin(dist, 1)])
+        assert np.array_equal(c[:, j], pick)
+        xh = c[:, j] * scales[j]
+        assert np.all(np.abs(x[:, j] - xh) <= 0.5 * scales[j] * (1 + 1e-5))
+
+
+def pin_lowrank_receiver(O):
+    """The low-rank receiver reproduces the sender's reconstruction bit for bit."""
+    traj = scaled_trajectory(64, 256, 3)
+    rng = np.random.default_rng(8)
+    for fb in (4, 32):
+        ah = np.empty(traj[0].shape, np.float32)
+        er = np.empty_like(ah)
+        O.init_state(traj[0], ah, er)
+        rx = ah.copy()
+        q = rng.standard_normal((256, 8)).astype(np.float32)
+        for t in (1, 2):
+            u, us, v, vs = O.lowrank_compress(traj[t], ah, er, q, 8, 2, fb)
+            O.lowrank_decompress(fb, u, us, v, vs, rx, 8)
+            assert np.array_equal(rx, ah)
+            assert np.array_equal(er, (f32(traj[t]) - ah).astype(np.float32))
+
+
+def pin_payload_size(O=None):
+    """Rank-32 INT4 payload of a 1024 x 3072 bf16 tensor: about 100x smaller
+    (Key results: 'about 100x compression (rank-32 INT4)')."""
+    m, n, k = 1024, 3072, 32
+    u, us, v, vs = (np.zeros(m * k // 2, np.uint8), np.zeros(k, np.float32),
+                    np.zeros(n * k // 2, np.uint8), np.zeros(k, np.float32))
+    payload = u.nbytes + us.nbytes + v.nbytes + vs.nbytes
+    assert payload == 65792
+    ratio = m * n * 2 / payload
+    assert 90 < ratio < 110, ratio
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
+
+
+def run_all(O) -> dict:
+    """Run every pin; returns {name: error string or None}."""
+    res = {}
+    for p in ALL_PINS:
+        try:
+            p(O)
+            res[p.__name__] = None
+        except Exception as e:  # noqa: BLE001 - a mutant may fail in any way
+            res[p.__name__] = f"{type(e).__name__}: {e}"[:200]
+    return res
+
+
+if __name__ == "__main__":
+    import json
+
+    sys.path.insert(0, _ROOT)
+    import oracle
+
+    path = sys.argv[1] if len(sys.argv) > 1 else oracle.LIB_PATH
+    print(json.dumps(run_all(oracle.Oracle(path))))
