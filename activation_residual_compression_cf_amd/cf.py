@@ -1,0 +1,226 @@
+"""Python binding of libcf (argument marshalling only).
+
+Every function here forwards to the C ABI declared in ``include/cf.h``; all
+arithmetic runs in the HIP kernels of ``libcf.so``.  PyTorch supplies device memory
+and streams.  Importing this module fails loudly when ``libcf.so`` is missing: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcf.so")
+
+CF_BF16, CF_F32 = 0, 1
+GROUP = 128
+
+STATUS = {0: "CF_OK", -1: "CF_E_NULL", -2: "CF_E_SHAPE", -3: "CF_E_ALIGN", -4: "CF_E_ARG",
+          -5: "CF_E_ALIAS", -6: "CF_E_WORKSPACE", -7: "CF_E_DEVICE", -8: "CF_E_HIP"}
+
+# name -> (restype, argtypes) ; i=int, l=int64, p=pointer, z=size_t
+_SIG = {
+    "cf_init_state": ("i", "ippplp"),
+    "cf_compress": ("i", "iippppplp"),
+    "cf_decompress": ("i", "ippplp"),
+    "cf_codes_bytes": ("l", "li"),
+    "cf_strerror": ("s", "i"),
+    "cf_abi_version": ("i", ""),
+}
+_CT = {"i": ctypes.c_int, "l": ctypes.c_int64, "p": ctypes.c_void_p, "z": ctypes.c_size_t,
+       "s": ctypes.c_char_p}
+
+
+class CFError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({strerror(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(the HIP library is required; there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIG.items():
+        f = getattr(lib, name)
+        f.restype = _CT[res]
+        f.argtypes = [_CT[c] for c in args]
+    return lib
+
+
+lib = _load()
+
+
+def strerror(status: int) -> str:
+    return lib.cf_strerror(status).decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise CFError(fn, rc)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libcf needs contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _act_dtype(a: torch.Tensor) -> int:
+    if a.dtype == torch.bfloat16:
+        return CF_BF16
+    if a.dtype == torch.float32:
+        return CF_F32
+    raise TypeError(f"activation dtype {a.dtype}: want torch.bfloat16 or torch.float32")
+
+
+def require_device() -> torch.device:
+    """cuda:0 if it is an MI355X (gfx950); raises otherwise."""
+    if not torch.cuda.is_available():
+        raise RuntimeError("no HIP device visible")
+    arch = torch.cuda.get_device_properties(0).gcnArchName
+    if not arch.startswith("gfx950"):
+        raise RuntimeError(f"device 0 is {arch}, libcf is built for gfx950 only")
+    return torch.device("cuda", 0)
+
+
+def codes_bytes(numel: int, bits: int) -> int:
+    n = lib.cf_codes_bytes(numel, bits)
+    if n < 0:
+        raise CFError("cf_codes_bytes", n)
+    return n
+
+
+@dataclass
+class SenderState:
+    """Sender-side state of one tensor (or slab): reconstruction and error buffer."""
+    ahat: torch.Tensor
+    err: torch.Tensor
+
+    @staticmethod
+    def create(numel: int, device=None) -> "SenderState":
+        device = device or require_device()
+        return SenderState(torch.empty(numel, dtype=torch.float32, device=device),
+                           torch.empty(numel, dtype=torch.float32, device=device))
+
+
+def init_state(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None = None, stream=None):
+    """Warmup: ahat = a, err = 0 (err None on the receiver)."""
+    _check("cf_init_state", lib.cf_init_state(_act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
+                                              a.numel(), _stream(stream)))
+
+
+def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
+             codes: torch.Tensor | None = None, scales: torch.Tensor | None = None, stream=None):
+    """One sender step; returns (codes uint8[numel*bits/8], scales fp32[numel/128])."""
+    n = a.numel()
+    if codes is None:
+        codes = torch.empty(max(n * bits // 8, 0), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty(max(n // GROUP, 0), dtype=torch.float32, device=a.device)
+    _check("cf_compress", lib.cf_compress(bits, _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
+                                          _ptr(codes), _ptr(scales), n, _stream(stream)))
+    return codes, scales
+
+
+def decompress(bits: int, codes: torch.Tensor, scales: torch.Tensor, ahat: torch.Tensor,
+               stream=None):
+    """Receiver step: ahat += decoded residual."""
+    _check("cf_decompress", lib.cf_decompress(bits, _ptr(codes), _ptr(scales), _ptr(ahat),
+                                              ahat.numel(), _stream(stream)))
+
+
+def _dev_ptr(t: torch.Tensor) -> int:
+    if not t.is_contiguous():
+        raise ValueError("libcf needs contiguous tensors")
+    return t.data_ptr()
+
+
+class Slab:
+    """1/2-bit state of ``count`` tensors of ``numel`` elements laid out back to back
+    (e.g. the K and V activations of every layer of one sequence-parallel shard).
+
+    ``compress``/``decompress``/``init`` issue one C-ABI call per ``per_call``
+    consecutive tensors (2 = one layer's K and V, the serving pattern; ``count`` = one
+    call for the whole step).  Pointers are computed once; each call only forwards
+    integers to libcf.
+    """
+
+    def __init__(self, count: int, numel: int, bits: int, device=None, receiver: bool = False):
+        if numel % GROUP:
+            raise ValueError("numel must be a multiple of 128")
+        device = device or require_device()
+        self.count, self.numel, self.bits = count, numel, bits
+        f32 = torch.float32
+        self.ahat = torch.empty((count, numel), dtype=f32, device=device)
+        self.err = None if receiver else torch.empty((count, numel), dtype=f32, device=device)
+        self.codes = torch.empty((count, numel * bits // 8), dtype=torch.uint8, device=device)
+        self.scales = torch.empty((count, numel // GROUP), dtype=f32, device=device)
+
+    def _chunks(self, per_call: int):
+        per_call = max(1, min(per_call, self.count))
+        for i in range(0, self.count, per_call):
+            yield i, min(per_call, self.count - i)
+
+    def init(self, a: torch.Tensor, per_call: int = 2, stream=None):
+        dt, s = _act_dtype(a), _stream(stream)
+        ab, esz = _dev_ptr(a), a.element_size()
+        hb = _dev_ptr(self.ahat)
+        eb = _dev_ptr(self.err) if self.err is not None else None
+        n = self.numel
+        for i, c in self._chunks(per_call):
+            _check("cf_init_state", lib.cf_init_state(
+                dt, ab + i * n * esz, hb + i * n * 4, None if eb is None else eb + i * n * 4,
+                c * n, s))
+
+    def compress(self, a: torch.Tensor, per_call: int = 2, stream=None, timer: list | None = None):
+        """Compress one step.  With ``timer`` a list, a pair of timing events recorded on
+        the launch stream just before and after every call is appended to it."""
+        if self.err is None:
+            raise RuntimeError("receiver slab has no error buffer")
+        if a.numel() != self.count * self.numel:
+            raise ValueError("activation slab has the wrong size")
+        dt, s, bits, n = _act_dtype(a), _stream(stream), self.bits, self.numel
+        ab, esz = _dev_ptr(a), a.element_size()
+        hb, eb = _dev_ptr(self.ahat), _dev_ptr(self.err)
+        cb, sb = _dev_ptr(self.codes), _dev_ptr(self.scales)
+        cbytes, ng = n * bits // 8, n // GROUP
+        f = lib.cf_compress
+        ts = None if timer is None else (torch.cuda.current_stream() if stream is None else stream)
+        for i, c in self._chunks(per_call):
+            if ts is not None:
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev0.record(ts)
+            rc = f(bits, dt, ab + i * n * esz, hb + i * n * 4, eb + i * n * 4, cb + i * cbytes,
+                   sb + i * ng * 4, c * n, s)
+            if rc:
+                raise CFError("cf_compress", rc)
+            if ts is not None:
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev1.record(ts)
+                timer.append((ev0, ev1))
+
+    def decompress(self, codes: torch.Tensor, scales: torch.Tensor, per_call: int = 2, stream=None):
+        s, bits, n = _stream(stream), self.bits, self.numel
+        cb, sb, hb = _dev_ptr(codes), _dev_ptr(scales), _dev_ptr(self.ahat)
+        cbytes, ng = n * bits // 8, n // GROUP
+        f = lib.cf_decompress
+        for i, c in self._chunks(per_call):
+            rc = f(bits, cb + i * cbytes, sb + i * ng * 4, hb + i * n * 4, c * n, s)
+            if rc:
+                raise CFError("cf_decompress", rc)

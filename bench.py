@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Throughput of CompactFusion's fused residual-compression + error-feedback step on
+one MI355X, on the FLUX-shaped sequence-parallel shard.
+
+Workload (synthetic stand-in for FLUX.1-dev activations, see ``gen``): 114 tensors per
+denoising step (57 layers x K,V), each 1024 tokens x 3072 channels bf16, per-channel
+lognormal scales with 1% outlier channels x20, drift 0.05 per step, 28 steps; step 0 is
+the warmup (the activation itself is sent), the rest are Compact-1bit compressed.
+
+A timed "step" compresses all 114 tensors of one denoising step with error feedback
+(one C-ABI call per layer: K and V as one 2-tensor slab), inputs resident in HBM.
+``value`` is GB/s of bf16 input activation (2 B x elements / time).  The JSON line also
+carries the roofline of the compress kernel (algorithmic bytes per launch / average
+launch time from HIP events around every launch), the oracle timed on the host cores
+on a bounded sample, and the other rows of the path (2-bit, decode, warmup init,
+CogVideoX-shaped shard) measured in the same process.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compress+EF GB/s of bf16 activation per GPU; % of HBM peak (FLUX shard)"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+# algorithmic bytes per element: a (bf16) read, ahat read + write, err write, codes, scales
+BYTES_PER_ELEM = {
+    "compress1": 2 + 4 + 4 + 4 + 1 / 8 + 4 / 128,
+    "compress2": 2 + 4 + 4 + 4 + 2 / 8 + 4 / 128,
+    "decode1": 4 + 4 + 1 / 8 + 4 / 128,
+    "decode2": 4 + 4 + 2 / 8 + 4 / 128,
+    "init": 2 + 4 + 4,
+}
+KERNEL_SRC = os.path.join(ROOT, "activation_residual_compression_cf_amd", "csrc", "cf_quant.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "compress_q1_flux_pmc.md")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None when the
+    kernel source changed since the counters were taken."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not b or h.group(1) != kernel_hash():
+        return None
+    return float(b.group(1))
+
+
+def time_calls(torch, fn, reps):
+    """Mean ms per call of fn() over reps calls, each bracketed by events."""
+    pairs = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return sum(x.elapsed_time(y) for x, y in pairs) / reps
+
+
+def cpu_baseline(wl, host_steps, bits, threads):
+    """The oracle, as it stands, on the host cores: full compressed steps of all tensors,
+    one tensor per task."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    O = oracle.default()
+    S = wl.slots
+    ahat = np.empty((S, wl.m, wl.n), np.float32)
+    err = np.empty_like(ahat)
+    for s in range(S):
+        O.init_state(host_steps[0][s], ahat[s], err[s])
+    nsteps = len(host_steps) - 1
+
+    def task(args):
+        t, s = args
+        O.compress(bits, host_steps[t][s], ahat[s], err[s])
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for t in range(1, nsteps + 1):
+            list(ex.map(task, [(t, s) for s in range(S)]))
+    dt = time.perf_counter() - t0
+    elems = nsteps * S * wl.m * wl.n
+    # single-thread figure on one tensor
+    a1 = np.empty((wl.m, wl.n), np.float32)
+    e1 = np.empty_like(a1)
+    O.init_state(host_steps[0][0], a1, e1)
+    t1 = time.perf_counter()
+    O.compress(bits, host_steps[1][0], a1, e1)
+    dt1 = time.perf_counter() - t1
+    return {
+        "value": round(elems * 2 / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{nsteps} compressed steps x {S} tensors of {wl.m}x{wl.n} bf16 "
+                  f"(Compact-{bits}bit, one tensor per task), {dt:.2f} s wall",
+        "single_thread_GBs": round(wl.m * wl.n * 2 / dt1 / 1e9, 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=25, help="timed denoising steps")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed compressed steps")
+    ap.add_argument("--per-call", type=int, default=2,
+                    help="tensors per C-ABI call (2 = one layer's K,V; 114 = whole step)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also launch one plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the compressor works on one sequence-parallel "
+              "rank's shard with no inter-GPU traffic; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    from activation_residual_compression_cf_amd import cf
+
+    dev = cf.require_device()
+    wl = gen.WORKLOADS["flux"]
+    numel = wl.numel
+    bits = 1
+    n_gen = min(1 + args.warmup + args.steps, wl.steps)
+    log(f"generating {n_gen} steps of {wl.slots} x {wl.m}x{wl.n} bf16 on the host")
+    t0 = time.perf_counter()
+    tr = gen.Trajectory(wl, args.seed)
+    steps_d = []
+    host_keep = []
+    n_host = 4  # steps kept on the host for the oracle baseline
+    for t in range(n_gen):
+        a = tr.next()
+        if t < n_host:
+            host_keep.append(a.copy())
+        steps_d.append(torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16))
+    torch.cuda.synchronize()
+    log(f"generated and uploaded in {time.perf_counter() - t0:.1f} s")
+
+    slab = cf.Slab(wl.slots, numel, bits, dev)
+    slab.init(steps_d[0], args.per_call)
+    compressed = list(range(1, n_gen))
+
+    def step_input(i):
+        return steps_d[compressed[i % len(compressed)]]
+
+    for i in range(args.warmup):
+        slab.compress(step_input(i), args.per_call)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events around every launch and around the region
+    launch_events = []
+
+    def stamp():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    per_call = max(1, min(args.per_call, wl.slots))
+    calls_per_step = -(-wl.slots // per_call)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start = stamp()
+    for i in range(args.steps):
+        a = step_input(args.warmup + i)
+        slab.compress(a, per_call, timer=launch_events)
+    end = stamp()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    step_bytes_act = wl.slots * numel * 2
+    value = step_bytes_act / (ms_per_step / 1e3) / 1e9
+
+    durs = [a.elapsed_time(b) for a, b in launch_events]
+    avg_launch_ms = sum(durs) / len(durs)
+    launch_elems = per_call * numel
+    algo_bytes = launch_elems * BYTES_PER_ELEM["compress1"]
+    achieved = algo_bytes / (avg_launch_ms / 1e3) / 1e9
+    traffic = counter_traffic()
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": "k_compress<1,bf16>",
+        "algorithmic_bytes_per_launch": int(algo_bytes),
+        "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+        "launches_timed": len(durs),
+    }
+    log(f"compress1 step {ms_per_step:.3f} ms, {value:.1f} GB/s act, launch {avg_launch_ms*1e3:.1f} us "
+        f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), wall {wall:.3f} s")
+
+    rows = {}
+    if not args.no_rows:
+        rows = secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = gen.default_threads()
+        log(f"oracle baseline on {threads} host threads")
+        cpu = cpu_baseline(wl, host_keep, bits, threads)
+        log(f"oracle: {cpu['value']} GB/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "FLUX-shaped shard, Compact-1bit: 114 tensors/step (57 layers x K,V) of "
+                        "1024 tokens x 3072 channels bf16, 28 steps, 1 warmup step",
+            "tensors_per_step": wl.slots,
+            "tokens": wl.m,
+            "channels": wl.n,
+            "bits": bits,
+            "group": 128,
+            "tensors_per_call": per_call,
+            "calls_per_step": calls_per_step,
+            "hbm_fraction_of_step": round(value * BYTES_PER_ELEM["compress1"] / 2 / HBM_PEAK_GBS, 4),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
+    """The other rows of the path, each timed with events over whole steps."""
+    numel = wl.numel
+    rows = {}
+    step_elems = wl.slots * numel
+
+    def row(name, ms, bytes_key, elems=step_elems):
+        gbs_act = elems * 2 / (ms / 1e3) / 1e9
+        hbm = elems * BYTES_PER_ELEM[bytes_key] / (ms / 1e3) / 1e9
+        rows[name] = {"ms_per_step": round(ms, 4), "act_GBs": round(gbs_act, 1),
+                      "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4)}
+        log(f"{name}: {ms:.3f} ms/step, {gbs_act:.0f} GB/s act, {hbm / HBM_PEAK_GBS:.1%} of HBM")
+
+    # 2-bit compress on the same shard
+    s2 = cf.Slab(wl.slots, numel, 2, dev)
+    s2.init(steps_d[0], per_call)
+    s2.compress(steps_d[compressed[0]], per_call)
+    it = iter(range(10 ** 9))
+    ms = time_calls(torch, lambda: s2.compress(steps_d[compressed[(next(it) + 1) % len(compressed)]],
+                                               per_call), 8)
+    row("compress2_flux", ms, "compress2")
+    # receiver decode, 1-bit and 2-bit (from the sender's last payload)
+    for bits, src in ((2, s2),):
+        rx = cf.Slab(wl.slots, numel, bits, dev, receiver=True)
+        rx.init(steps_d[0], per_call)
+        ms = time_calls(torch, lambda: rx.decompress(src.codes, src.scales, per_call), 8)
+        row(f"decode{bits}_flux", ms, f"decode{bits}")
+        del rx
+    s1 = cf.Slab(wl.slots, numel, 1, dev)
+    s1.init(steps_d[0], per_call)
+    s1.compress(steps_d[compressed[0]], per_call)
+    rx = cf.Slab(wl.slots, numel, 1, dev, receiver=True)
+    rx.init(steps_d[0], per_call)
+    ms = time_calls(torch, lambda: rx.decompress(s1.codes, s1.scales, per_call), 8)
+    row("decode1_flux", ms, "decode1")
+    ms = time_calls(torch, lambda: s1.init(steps_d[0], per_call), 8)
+    row("init_flux", ms, "init")
+    del s1, s2, rx
+    # one-call-per-step pattern for the headline kernel
+    s1 = cf.Slab(wl.slots, numel, 1, dev)
+    s1.init(steps_d[0], wl.slots)
+    it2 = iter(range(10 ** 9))
+    ms = time_calls(torch, lambda: s1.compress(steps_d[compressed[next(it2) % len(compressed)]],
+                                               wl.slots), 8)
+    row("compress1_flux_one_call", ms, "compress1")
+    del s1
+    torch.cuda.empty_cache()
+    # CogVideoX-shaped shard, Compact-2bit
+    cw = gen.WORKLOADS["cogvideo"]
+    tr = gen.Trajectory(cw, 0)
+    cs = [torch.from_numpy(tr.next().view(np.int16)).to(dev).view(torch.bfloat16) for _ in range(4)]
+    sc = cf.Slab(cw.slots, cw.numel, 2, dev)
+    sc.init(cs[0], per_call)
+    sc.compress(cs[1], per_call)
+    it3 = iter(range(10 ** 9))
+    ms = time_calls(torch, lambda: sc.compress(cs[2 + next(it3) % 2], per_call), 8)
+    row("compress2_cogvideo", ms, "compress2", cw.slots * cw.numel)
+    del sc, cs
+    torch.cuda.empty_cache()
+    return rows
+
+
+if __name__ == "__main__":
+    main()

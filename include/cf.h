@@ -1,0 +1,119 @@
+/*
+ * cf.h - C ABI of libcf: CompactFusion step-wise activation residual compression
+ * with sender-side error feedback, on MI355X (gfx950).
+ *
+ * Method: "Accelerating Parallel Diffusion Model Serving with Residual
+ * Compression" (CompactFusion summary), section Approach: at every denoising
+ * step each layer activation is sent as the compressed difference from the
+ * previous *reconstructed* activation, the sender keeps error feedback so the
+ * quantization error does not accumulate, and a low-rank variant with INT4
+ * factors reaches extreme ratios; the measured-effects table names the
+ * Compact-1bit, Compact-2bit and Compact-Lowrank variants and the warmup steps.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer on the current HIP device, allocated and
+ *     owned by the caller, who keeps it alive until the stream work is done.
+ *     The library allocates nothing in these calls and keeps no pointer after
+ *     a call returns.
+ *   - Calls are stream-ordered and asynchronous: CF_OK means "validated and
+ *     enqueued on `stream`" (a hipStream_t; NULL = the null stream).  A fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - Every argument is validated before anything is enqueued, so a call that
+ *     returns an error has written nothing (a half-applied state update would
+ *     corrupt the error feedback).
+ *   - Activations `a` are bf16 (CF_BF16, raw 16-bit storage) or fp32 (CF_F32),
+ *     row-major; the reconstruction `ahat` and the error buffer `err` are fp32.
+ *     State lives only in caller buffers, so a checkpoint is a copy of them.
+ *   - A group is CF_GROUP = 128 contiguous elements; `numel` must be a positive
+ *     multiple of 128.  Several tensors laid out back to back may be passed as
+ *     one call (one "slab"), since no group straddles two tensors when every
+ *     tensor's size is a multiple of 128.
+ *   - Every pointer must be 16-byte aligned, except `scales` (one float per
+ *     group), which needs 4-byte alignment; input and output ranges must not
+ *     overlap.
+ *   - Results are deterministic: no atomics, fixed reduction orders.
+ *   - Calls on different streams with disjoint buffers may run concurrently.
+ *   - Non-finite inputs give unspecified (but memory-safe) results.
+ */
+#ifndef CF_H
+#define CF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes: 0 on success, negative on error. */
+enum {
+    CF_OK = 0,
+    CF_E_NULL = -1,      /* a required pointer is NULL */
+    CF_E_SHAPE = -2,     /* numel / m / n / rank / batch out of range */
+    CF_E_ALIGN = -3,     /* a pointer is misaligned (16 bytes; scales 4 bytes) */
+    CF_E_ARG = -4,       /* bits, dtype, factor_bits or iters not supported */
+    CF_E_ALIAS = -5,     /* an output range overlaps another operand */
+    CF_E_WORKSPACE = -6, /* workspace missing or too small */
+    CF_E_DEVICE = -7,    /* current device is not gfx950 */
+    CF_E_HIP = -8        /* the HIP runtime refused a launch */
+};
+
+enum { CF_BF16 = 0, CF_F32 = 1 };
+
+#define CF_GROUP 128
+
+/*
+ * Warmup / initialisation (measured-effects table: "1-step warmup", "2 warmup
+ * steps").  During the first W steps the activation itself is sent and both
+ * sides take it as their reconstruction:  ahat[i] = a[i]  and, when `err` is
+ * not NULL (the sender), err[i] = 0.  The receiver passes err = NULL.
+ *   a:    numel elements of `a_dtype`
+ *   ahat: numel fp32 (out)      err: numel fp32 (out) or NULL
+ */
+int cf_init_state(int a_dtype, const void* a, float* ahat, float* err, int64_t numel,
+                  void* stream);
+
+/*
+ * Sender step, Compact-1bit / Compact-2bit (Approach: residual against the
+ * previous reconstruction with sender-side error feedback).  Per group g of 128
+ * contiguous elements:
+ *   r = a - ahat                                         (fp32)
+ *   bits = 1: s = mean|r| (16 partial sums of 8 consecutive |r|, combined by the
+ *             butterfly L_j += L_{j^o} for o = 8, 4, 2, 1, then / 128);
+ *             code = (r < 0);  d = code ? -s : s
+ *   bits = 2: s = max|r| / 1.5 (IEEE division);  sign = (r < 0),
+ *             mag = (|r| > s);  code = sign | mag << 1;
+ *             d = +-(mag ? 1.5*s : 0.5*s)   (levels {-1.5,-0.5,0.5,1.5}*s)
+ *   ahat = ahat + d;   err = a - ahat        (each operation rounded once)
+ *   codes: numel*bits/8 bytes, LSB first, groups back to back (16*bits bytes
+ *          per group); scales: numel/128 fp32, one per group.
+ *   a: in; ahat: in/out; err: out; codes, scales: out.
+ */
+int cf_compress(int bits, int a_dtype, const void* a, float* ahat, float* err, uint8_t* codes,
+                float* scales, int64_t numel, void* stream);
+
+/*
+ * Receiver step: decodes codes/scales with exactly the sender's expression for
+ * d and applies ahat = ahat + d, so the receiver's reconstruction equals the
+ * sender's bit for bit (Approach: the receiver rebuilds the activation from
+ * the transmitted residuals).
+ *   codes, scales: in (as produced by cf_compress); ahat: in/out.
+ */
+int cf_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat, int64_t numel,
+                  void* stream);
+
+/* Bytes of packed codes for numel elements at `bits` per element (numel*bits/8),
+ * or a negative status for invalid arguments. */
+int64_t cf_codes_bytes(int64_t numel, int bits);
+
+/* Human-readable name of a status code (static storage). */
+const char* cf_strerror(int status);
+
+/* ABI version of this header: 1. */
+int cf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CF_H */

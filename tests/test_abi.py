@@ -1,0 +1,116 @@
+"""The C ABI library: it loads, exports every symbol the headers declare, and its
+validation (which runs before any HIP call) rejects bad arguments.  No compute call
+is made here: pointers are fake addresses that are never dereferenced, and a fully
+valid call stops at the device check where there is no gfx950."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "activation_residual_compression_cf_amd", "libcf.so")
+
+CF_OK, CF_E_NULL, CF_E_SHAPE, CF_E_ALIGN, CF_E_ARG, CF_E_ALIAS, CF_E_WORKSPACE, CF_E_DEVICE = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+
+
+def declared_symbols():
+    syms = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        syms |= set(re.findall(r"^\s*[a-z_][\w\s\*]*?\b(cf_\w+)\s*\(", text, flags=re.M))
+    return sorted(syms)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail("libcf.so is not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB)
+    return lib
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for want in ("cf_init_state", "cf_compress", "cf_decompress", "cf_strerror"):
+        assert want in syms
+
+
+def test_every_declared_symbol_is_exported(L):
+    for s in declared_symbols():
+        assert hasattr(L, s), f"{s} declared in include/ but not exported by libcf.so"
+
+
+def test_no_torch_in_the_library():
+    # the boundary carries plain pointers and sizes only
+    out = os.popen(f"nm -D --defined-only {LIB}").read()
+    assert "torch" not in out and "at::" not in out
+
+
+def test_strerror_and_version(L):
+    L.cf_strerror.restype = ctypes.c_char_p
+    for code in range(0, -9, -1):
+        assert L.cf_strerror(code)
+    assert L.cf_abi_version() == 1
+
+
+def test_codes_bytes(L):
+    L.cf_codes_bytes.restype = ctypes.c_int64
+    L.cf_codes_bytes.argtypes = [ctypes.c_int64, ctypes.c_int]
+    assert L.cf_codes_bytes(1024 * 3072, 1) == 393216
+    assert L.cf_codes_bytes(1024 * 3072, 2) == 786432
+    assert L.cf_codes_bytes(2925 * 1920, 2) == 1404000
+    assert L.cf_codes_bytes(100, 1) == CF_E_SHAPE
+    assert L.cf_codes_bytes(128, 3) == CF_E_ARG
+
+
+def _compress(L, bits=1, dt=0, a=0x10000, ah=0x1000000, e=0x2000000, c=0x3000000, s=0x4000000,
+              n=1280):
+    L.cf_compress.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5 + [
+        ctypes.c_int64, ctypes.c_void_p]
+    return L.cf_compress(bits, dt, P(a) if a else None, P(ah) if ah else None,
+                         P(e) if e else None, P(c) if c else None, P(s) if s else None, n, None)
+
+
+def test_compress_validation(L):
+    assert _compress(L, bits=3) == CF_E_ARG
+    assert _compress(L, dt=2) == CF_E_ARG
+    assert _compress(L, a=0) == CF_E_NULL
+    assert _compress(L, s=0) == CF_E_NULL
+    assert _compress(L, n=0) == CF_E_SHAPE
+    assert _compress(L, n=-128) == CF_E_SHAPE
+    assert _compress(L, n=1000) == CF_E_SHAPE
+    assert _compress(L, n=(1 << 40) + 128) == CF_E_SHAPE
+    assert _compress(L, a=0x10008) == CF_E_ALIGN
+    assert _compress(L, c=0x3000004) == CF_E_ALIGN
+    assert _compress(L, s=0x4000002) == CF_E_ALIGN
+    assert _compress(L, s=0x4000004) == CF_E_DEVICE  # scales need 4-byte alignment only
+    assert _compress(L, e=0x1000000 + 1280 * 4 - 16) == CF_E_ALIAS     # err overlaps ahat's tail
+    assert _compress(L, a=0x1000000 - 16) == CF_E_ALIAS               # a runs into ahat
+    assert _compress(L, c=0x4000000) == CF_E_ALIAS                    # codes == scales
+    assert _compress(L, e=0x1000000 + 1280 * 4) == CF_E_DEVICE        # adjacent is fine
+    assert _compress(L) == CF_E_DEVICE  # valid: stops at the device check (no gfx950 here)
+
+
+def test_init_and_decompress_validation(L):
+    L.cf_init_state.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int64,
+                                                                          ctypes.c_void_p]
+    L.cf_decompress.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 3 + [ctypes.c_int64,
+                                                                          ctypes.c_void_p]
+    assert L.cf_init_state(5, P(0x10000), P(0x100000), None, 128, None) == CF_E_ARG
+    assert L.cf_init_state(0, None, P(0x100000), None, 128, None) == CF_E_NULL
+    assert L.cf_init_state(0, P(0x10000), P(0x100000), None, 64, None) == CF_E_SHAPE
+    assert L.cf_init_state(0, P(0x10000), P(0x100004), None, 128, None) == CF_E_ALIGN
+    assert L.cf_init_state(1, P(0x10000), P(0x10000 + 256), None, 128, None) == CF_E_ALIAS
+    assert L.cf_init_state(0, P(0x10000), P(0x100000), None, 128, None) == CF_E_DEVICE
+    assert L.cf_decompress(0, P(0x10000), P(0x20000), P(0x30000), 128, None) == CF_E_ARG
+    assert L.cf_decompress(1, None, P(0x20000), P(0x30000), 128, None) == CF_E_NULL
+    assert L.cf_decompress(1, P(0x10000), P(0x20000), P(0x30000), 129, None) == CF_E_SHAPE
+    assert L.cf_decompress(2, P(0x10000), P(0x20000), P(0x20000), 128, None) == CF_E_ALIAS
+    assert L.cf_decompress(2, P(0x10000), P(0x20000), P(0x30000), 128, None) == CF_E_DEVICE
