@@ -78,8 +78,8 @@ int cf_init_state(int a_dtype, const void* a, float* ahat, float* err, int64_t n
  * previous reconstruction with sender-side error feedback).  Per group g of 128
  * contiguous elements:
  *   r = a - ahat                                         (fp32)
- *   bits = 1: s = mean|r| (16 partial sums of 8 consecutive |r|, combined by the
- *             butterfly L_j += L_{j^o} for o = 8, 4, 2, 1, then / 128);
+ *   bits = 1: s = mean|r| (32 partial sums of 4 consecutive |r|, combined by the
+ *             butterfly L_j += L_{j^o} for o = 16, 8, 4, 2, 1, then / 128);
  *             code = (r < 0);  d = code ? -s : s
  *   bits = 2: s = max|r| / 1.5 (IEEE division);  sign = (r < 0),
  *             mag = (|r| > s);  code = sign | mag << 1;

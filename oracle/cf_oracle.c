@@ -20,8 +20,8 @@
  * The pages fix neither group size, scale rule, code layout nor precision; the
  * readings taken here are:
  *   - groups of 128 contiguous elements; 1-bit: code = (r < 0), scale = mean|r|
- *     (summed as 16 left-to-right partial sums of 8 elements, combined by the
- *     butterfly L_j += L_{j^o}, o = 8, 4, 2, 1, then divided by 128);
+ *     (summed as 32 left-to-right partial sums of 4 elements, combined by the
+ *     butterfly L_j += L_{j^o}, o = 16, 8, 4, 2, 1, then divided by 128);
  *     2-bit: scale s = max|r| / 1.5, levels {-1.5, -0.5, 0.5, 1.5} * s chosen
  *     by round-to-nearest with ties to the inner level, code bit0 = sign,
  *     bit1 = magnitude; codes packed LSB-first, 8 or 4 per byte;
@@ -77,14 +77,14 @@ static int check_common(int bits, int dtype, int64_t numel) {
 
 /* 1-bit scale: mean of |r| in the fixed summation order described above. */
 static float scale_1bit(const float* r) {
-    float L[16], nxt[16];
-    for (int j = 0; j < 16; ++j) {
-        float s = fabsf(r[8 * j]);
-        for (int i = 1; i < 8; ++i) s = s + fabsf(r[8 * j + i]);
+    float L[32], nxt[32];
+    for (int j = 0; j < 32; ++j) {
+        float s = fabsf(r[4 * j]);
+        for (int i = 1; i < 4; ++i) s = s + fabsf(r[4 * j + i]);
         L[j] = s;
     }
-    for (int o = 8; o >= 1; o >>= 1) {
-        for (int j = 0; j < 16; ++j) nxt[j] = L[j] + L[j ^ o];
+    for (int o = 16; o >= 1; o >>= 1) {
+        for (int j = 0; j < 32; ++j) nxt[j] = L[j] + L[j ^ o];
         memcpy(L, nxt, sizeof L);
     }
     return L[0] / 128.0f;

@@ -31,7 +31,7 @@ MUTANTS = [
      "for (int i = 0; i < CFO_GROUP; ++i) r[i] = act(dtype, a, base + i);"),
     ("q1_mean_divisor", "return L[0] / 128.0f;", "return L[0] / 127.0f;"),
     ("q1_butterfly_index", "nxt[j] = L[j] + L[j ^ o];", "nxt[j] = L[j] + L[j ^ (o >> 1)];"),
-    ("q1_partial_sum_stride", "s = s + fabsf(r[8 * j + i]);", "s = s + fabsf(r[8 * i + j]);"),
+    ("q1_partial_sum_stride", "s = s + fabsf(r[4 * j + i]);", "s = s + fabsf(r[4 * i + j]);"),
     ("q1_code_sign", "c = r[i] < 0.0f ? 1u : 0u;", "c = r[i] > 0.0f ? 1u : 0u;"),
     ("q1_bit_order", "gcodes[i >> 3] |= (uint8_t)(c << (i & 7));",
      "gcodes[i >> 3] |= (uint8_t)(c << (7 - (i & 7)));"),
