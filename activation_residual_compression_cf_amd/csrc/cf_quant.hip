@@ -6,60 +6,52 @@
 // previous reconstruction, sender-side error feedback) and the measured-effects
 // table (Compact-1bit, Compact-2bit, warmup steps).
 //
-// Work mapping (wave64): a group of 128 contiguous elements is owned by one
-// 16-lane row of a wavefront, each lane holding 8 consecutive elements, so one
-// wave instruction moves 4 whole groups (1 KiB of bf16, 2 KiB of fp32 state) with
-// 16-byte per-lane accesses.  The group reduction (sum or max of |r|) runs over
-// the 16 lanes of the row with an xor butterfly (8, 4, 2, 1); every lane ends with
-// the same value.  The whole step - residual, scale, codes, packing,
-// reconstruction update and error - is one pass: each element's activation and
-// reconstruction are read once and the reconstruction and error written once.
-// Every block covers 16 * TILES groups with TILES independent wave-tiles in
-// flight per wave; there are no atomics and no inter-block communication.
+// Work mapping (wave64).  A wave tile is 2*IPS consecutive groups (256*IPS
+// elements).  Wave instruction k (0 <= k < IPS) covers elements
+// [256k, 256k + 256) of the tile: lane j holds the 4 consecutive elements
+// 256k + 4j .. 256k + 4j + 3, so every load and store instruction touches one
+// contiguous span (1 KiB of fp32 state, 512 B of bf16 activation) and each half
+// wave (32 lanes) owns one whole group of 128 elements.  The group reduction
+// (sum or max of |r|) is a 5-step xor butterfly (16, 8, 4, 2, 1) inside the half
+// wave; every lane ends with the same value.  Activations and state are read, and
+// state written, with non-temporal accesses: each byte is touched once per step,
+// so nothing is worth keeping in L2 and the end-of-kernel write-back stays short.
+// One pass per element: the activation and reconstruction are read once, the
+// reconstruction and error written once, codes and the scale written once per
+// group.  No atomics, no inter-block communication.
+//
+// Launch shape: large calls (a whole denoising step of many tensors) use one
+// instruction per stream per tile and 256-thread blocks; small calls (a single
+// layer) use two instructions per tile and 128-thread blocks, which keeps more
+// bytes in flight per wave when the grid alone cannot fill the chip for long.
 //
 // Numerics: fp32 throughout, built with -ffp-contract=off so that every add and
-// multiply rounds once, in the order written; the 2-bit scale uses IEEE
-// division.
+// multiply rounds once, in the order written; the 2-bit scale uses IEEE division.
 
 #include "cf_internal.h"
 
 namespace cf {
 namespace {
 
-constexpr int kBlock = 256;  // 4 waves
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef unsigned vu2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// 8 consecutive activations at element offset `off`, widened to fp32 (exact).
-__device__ __forceinline__ void load_act8(const uint16_t* __restrict__ a, int64_t off, float (&x)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(a + off);
-    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
-    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+__device__ __forceinline__ vf4 ld_nt(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, vf4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<vf4*>(p));
 }
 
-__device__ __forceinline__ void load_act8(const float* __restrict__ a, int64_t off, float (&x)[8]) {
-    const float4 v0 = *reinterpret_cast<const float4*>(a + off);
-    const float4 v1 = *reinterpret_cast<const float4*>(a + off + 4);
-    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+// 4 consecutive activations at element offset `off`, widened to fp32 (exact).
+__device__ __forceinline__ vf4 load_act4(const uint16_t* __restrict__ a, int64_t off) {
+    const vu2 w = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(a + off));
+    return vf4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
 }
+__device__ __forceinline__ vf4 load_act4(const float* __restrict__ a, int64_t off) { return ld_nt(a + off); }
 
-__device__ __forceinline__ void load_f8(const float* __restrict__ p, int64_t off, float (&x)[8]) {
-    const float4 v0 = *reinterpret_cast<const float4*>(p + off);
-    const float4 v1 = *reinterpret_cast<const float4*>(p + off + 4);
-    x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-    x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-}
-
-__device__ __forceinline__ void store_f8(float* __restrict__ p, int64_t off, const float (&x)[8]) {
-    *reinterpret_cast<float4*>(p + off) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(p + off + 4) = make_float4(x[4], x[5], x[6], x[7]);
-}
-
-// Value held by lane (this lane ^ mask); masks < 16 stay inside the 16-lane row.
+// Value held by lane (this lane ^ mask) / (this lane + delta), as 32-bit words.
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ uint32_t down_lane(uint32_t v, int delta) {
     return static_cast<uint32_t>(__shfl_down(static_cast<int>(v), delta, 64));
@@ -76,169 +68,180 @@ __device__ __forceinline__ float dequant(uint32_t c, float s) {
     }
 }
 
-template <int BITS, typename ActT, int TILES>
-__global__ __launch_bounds__(kBlock) void k_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
-                                                      float* __restrict__ err, uint8_t* __restrict__ codes,
-                                                      float* __restrict__ scales, int64_t ngroups) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int sub = lane & 15;  // lane within the group's 16-lane row
-    const int64_t gbase = static_cast<int64_t>(blockIdx.x) * (16 * TILES) + wave * 4 + (lane >> 4);
+template <int BITS>
+__device__ __forceinline__ vf4 dequant4(uint32_t c, float s) {
+    return vf4{dequant<BITS>(c, s), dequant<BITS>(c >> BITS, s), dequant<BITS>(c >> (2 * BITS), s),
+               dequant<BITS>(c >> (3 * BITS), s)};
+}
 
-    float x[TILES][8], h[TILES][8];
-    int64_t gi[TILES];
-    bool ok[TILES];
+template <int BITS, typename ActT, int IPS, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
+                                                     float* __restrict__ err, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scales, int64_t ngroups) {
+    constexpr int kWaves = BLOCK / 64;
+    const int lane = threadIdx.x & 63;
+    const int hl = lane & 31;  // lane within the half wave that owns a group
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    const int64_t g0 = tile * (2 * IPS) + (lane >> 5);
+    if (tile * (2 * IPS) >= ngroups) return;  // uniform per wave
+
+    vf4 x[IPS], h[IPS];
+    int64_t gi[IPS];
+    bool ok[IPS];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        const int64_t g = gbase + 16 * t;
-        ok[t] = g < ngroups;
-        gi[t] = ok[t] ? g : ngroups - 1;  // out-of-range rows reload the last group; stores skipped
-        const int64_t off = gi[t] * kGroup + sub * 8;
-        load_act8(a, off, x[t]);
-        load_f8(ahat, off, h[t]);
+    for (int k = 0; k < IPS; ++k) {
+        const int64_t g = g0 + 2 * k;
+        ok[k] = g < ngroups;
+        gi[k] = ok[k] ? g : ngroups - 1;  // ragged tail: reload the last group, skip the stores
+        const int64_t off = gi[k] * kGroup + hl * 4;
+        x[k] = load_act4(a, off);
+        h[k] = ld_nt(ahat + off);
     }
 
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        float r[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = x[t][i] - h[t][i];
-
+    for (int k = 0; k < IPS; ++k) {
+        const vf4 r = x[k] - h[k];
         float s;
-        uint32_t code = 0;
+        uint32_t code;
         if constexpr (BITS == 1) {
-            float L = fabsf(r[0]);
-#pragma unroll
-            for (int i = 1; i < 8; ++i) L = L + fabsf(r[i]);
+            float L = fabsf(r.x);
+            L = L + fabsf(r.y);
+            L = L + fabsf(r.z);
+            L = L + fabsf(r.w);
+            L = L + xor_lane(L, 16);
             L = L + xor_lane(L, 8);
             L = L + xor_lane(L, 4);
             L = L + xor_lane(L, 2);
             L = L + xor_lane(L, 1);
             s = L / 128.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) code |= (r[i] < 0.0f ? 1u : 0u) << i;
+            code = (r.x < 0.0f ? 1u : 0u) | (r.y < 0.0f ? 2u : 0u) | (r.z < 0.0f ? 4u : 0u) |
+                   (r.w < 0.0f ? 8u : 0u);
         } else {
-            float M = fabsf(r[0]);
-#pragma unroll
-            for (int i = 1; i < 8; ++i) M = fmaxf(M, fabsf(r[i]));
+            float M = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
+            M = fmaxf(M, xor_lane(M, 16));
             M = fmaxf(M, xor_lane(M, 8));
             M = fmaxf(M, xor_lane(M, 4));
             M = fmaxf(M, xor_lane(M, 2));
             M = fmaxf(M, xor_lane(M, 1));
             s = M / 1.5f;
+            code = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4; ++i) {
                 const uint32_t sign = r[i] < 0.0f ? 1u : 0u;
                 const uint32_t mag = fabsf(r[i]) > s ? 1u : 0u;
                 code |= (sign | (mag << 1)) << (2 * i);
             }
         }
+        const vf4 hn = h[k] + dequant4<BITS>(code, s);
+        const vf4 e = x[k] - hn;
 
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            h[t][i] = h[t][i] + dequant<BITS>(code >> (BITS * i), s);
-            e[i] = x[t][i] - h[t][i];
-        }
-
-        // Pack: 1-bit -> 4 lanes' bytes per dword, 2-bit -> 2 lanes' halfwords per dword.
-        uint32_t packed;
+        // Gather the group's codes into dwords: 1-bit lanes hold a nibble (8 lanes
+        // per dword), 2-bit lanes a byte (4 lanes per dword).
+        uint32_t w;
         if constexpr (BITS == 1) {
-            packed = code | (down_lane(code, 1) << 8) | (down_lane(code, 2) << 16) | (down_lane(code, 3) << 24);
+            w = code | (down_lane(code, 1) << 4);
+            w = w | (down_lane(w, 2) << 8);
+            w = w | (down_lane(w, 4) << 16);
         } else {
-            packed = code | (down_lane(code, 1) << 16);
+            w = code | (down_lane(code, 1) << 8);
+            w = w | (down_lane(w, 2) << 16);
         }
 
-        if (ok[t]) {
-            const int64_t off = gi[t] * kGroup + sub * 8;
-            store_f8(ahat, off, h[t]);
-            store_f8(err, off, e);
+        if (ok[k]) {
+            const int64_t off = gi[k] * kGroup + hl * 4;
+            st_nt(ahat + off, hn);
+            st_nt(err + off, e);
             if constexpr (BITS == 1) {
-                if ((sub & 3) == 0) *reinterpret_cast<uint32_t*>(codes + gi[t] * 16 + sub) = packed;
+                if ((hl & 7) == 0) *reinterpret_cast<uint32_t*>(codes + gi[k] * 16 + (hl >> 1)) = w;
             } else {
-                if ((sub & 1) == 0) *reinterpret_cast<uint32_t*>(codes + gi[t] * 32 + sub * 2) = packed;
+                if ((hl & 3) == 0) *reinterpret_cast<uint32_t*>(codes + gi[k] * 32 + hl) = w;
             }
-            if (sub == 0) scales[gi[t]] = s;
+            if (hl == 0) scales[gi[k]] = s;
         }
     }
 }
 
-template <int BITS, int TILES>
-__global__ __launch_bounds__(kBlock) void k_decompress(const uint8_t* __restrict__ codes,
-                                                        const float* __restrict__ scales,
-                                                        float* __restrict__ ahat, int64_t ngroups) {
+template <int BITS, int IPS, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict__ codes,
+                                                       const float* __restrict__ scales,
+                                                       float* __restrict__ ahat, int64_t ngroups) {
+    constexpr int kWaves = BLOCK / 64;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int sub = lane & 15;
-    const int64_t gbase = static_cast<int64_t>(blockIdx.x) * (16 * TILES) + wave * 4 + (lane >> 4);
+    const int hl = lane & 31;
+    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    const int64_t g0 = tile * (2 * IPS) + (lane >> 5);
+    if (tile * (2 * IPS) >= ngroups) return;
 
-    float h[TILES][8], s[TILES];
-    uint32_t code[TILES];
-    int64_t gi[TILES];
-    bool ok[TILES];
+    vf4 h[IPS];
+    float s[IPS];
+    uint32_t code[IPS];
+    int64_t gi[IPS];
+    bool ok[IPS];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-        const int64_t g = gbase + 16 * t;
-        ok[t] = g < ngroups;
-        gi[t] = ok[t] ? g : ngroups - 1;
+    for (int k = 0; k < IPS; ++k) {
+        const int64_t g = g0 + 2 * k;
+        ok[k] = g < ngroups;
+        gi[k] = ok[k] ? g : ngroups - 1;
         if constexpr (BITS == 1) {
-            code[t] = codes[gi[t] * 16 + sub];
+            code[k] = (static_cast<uint32_t>(codes[gi[k] * 16 + (hl >> 1)]) >> ((hl & 1) * 4)) & 0xFu;
         } else {
-            code[t] = *reinterpret_cast<const uint16_t*>(codes + gi[t] * 32 + sub * 2);
+            code[k] = codes[gi[k] * 32 + hl];
         }
-        s[t] = scales[gi[t]];
-        load_f8(ahat, gi[t] * kGroup + sub * 8, h[t]);
+        s[k] = scales[gi[k]];
+        h[k] = ld_nt(ahat + gi[k] * kGroup + hl * 4);
     }
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[t][i] = h[t][i] + dequant<BITS>(code[t] >> (BITS * i), s[t]);
-        if (ok[t]) store_f8(ahat, gi[t] * kGroup + sub * 8, h[t]);
+    for (int k = 0; k < IPS; ++k) {
+        const vf4 hn = h[k] + dequant4<BITS>(code[k], s[k]);
+        if (ok[k]) st_nt(ahat + gi[k] * kGroup + hl * 4, hn);
     }
 }
 
-// Warmup: ahat = a (widened), err = 0 when err is given.  8 elements per thread.
+// Warmup: ahat = a (widened), err = 0 when err is given.  4 elements per thread.
 template <typename ActT>
-__global__ __launch_bounds__(kBlock) void k_init(const ActT* __restrict__ a, float* __restrict__ ahat,
-                                                  float* __restrict__ err, int64_t nvec) {
-    const int64_t v = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (v >= nvec) return;
-    float x[8];
-    load_act8(a, v * 8, x);
-    store_f8(ahat, v * 8, x);
-    if (err) {
-        const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        store_f8(err, v * 8, z);
-    }
+__global__ __launch_bounds__(256) void k_init(const ActT* __restrict__ a, float* __restrict__ ahat,
+                                               float* __restrict__ err, int64_t nquads) {
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (q >= nquads) return;
+    st_nt(ahat + q * 4, load_act4(a, q * 4));
+    if (err) st_nt(err + q * 4, vf4{0.f, 0.f, 0.f, 0.f});
 }
 
-constexpr int kTiles = 2;
+// Calls of at least this many groups (about 8 FLUX-shard tensors) take the large shape.
+constexpr int64_t kLargeCall = int64_t(1) << 17;
+
+template <typename K>
+hipError_t launch(K kernel, int64_t ngroups, int ips, int block, void** args, hipStream_t stream) {
+    const int64_t tiles = (ngroups + 2 * ips - 1) / (2 * ips);
+    const int64_t waves_per_block = block / 64;
+    const int64_t blocks = (tiles + waves_per_block - 1) / waves_per_block;
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
+                           dim3(block), args, 0, stream);
+}
 
 template <int BITS, typename ActT>
 hipError_t run_compress(const ActT* a, float* ahat, float* err, uint8_t* codes, float* scales,
                         int64_t ngroups, hipStream_t stream) {
-    const int64_t blocks = (ngroups + 16 * kTiles - 1) / (16 * kTiles);
     void* args[] = {&a, &ahat, &err, &codes, &scales, &ngroups};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_compress<BITS, ActT, kTiles>),
-                           dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args, 0, stream);
+    if (ngroups >= kLargeCall) return launch(&k_compress<BITS, ActT, 1, 256>, ngroups, 1, 256, args, stream);
+    return launch(&k_compress<BITS, ActT, 2, 128>, ngroups, 2, 128, args, stream);
 }
 
 template <int BITS>
 hipError_t run_decompress(const uint8_t* codes, const float* scales, float* ahat, int64_t ngroups,
                           hipStream_t stream) {
-    const int64_t blocks = (ngroups + 16 * kTiles - 1) / (16 * kTiles);
     void* args[] = {&codes, &scales, &ahat, &ngroups};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_decompress<BITS, kTiles>),
-                           dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args, 0, stream);
+    if (ngroups >= kLargeCall) return launch(&k_decompress<BITS, 1, 256>, ngroups, 1, 256, args, stream);
+    return launch(&k_decompress<BITS, 2, 128>, ngroups, 2, 128, args, stream);
 }
 
 template <typename ActT>
 hipError_t run_init(const ActT* a, float* ahat, float* err, int64_t numel, hipStream_t stream) {
-    int64_t nvec = numel / 8;
-    const int64_t blocks = (nvec + kBlock - 1) / kBlock;
-    void* args[] = {&a, &ahat, &err, &nvec};
+    int64_t nquads = numel / 4;
+    const int64_t blocks = (nquads + 255) / 256;
+    void* args[] = {&a, &ahat, &err, &nquads};
     return hipLaunchKernel(reinterpret_cast<const void*>(&k_init<ActT>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(kBlock), args, 0, stream);
+                           dim3(256), args, 0, stream);
 }
 
 }  // namespace
