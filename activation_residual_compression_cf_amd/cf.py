@@ -27,6 +27,9 @@ _SIG = {
     "cf_init_state": ("i", "ippplp"),
     "cf_compress": ("i", "iippppplp"),
     "cf_decompress": ("i", "ippplp"),
+    "cf_lowrank_compress": ("i", "ipppllii" "iipppppp" "zp"),
+    "cf_lowrank_decompress": ("i", "ipppp" "pllii" "p"),
+    "cf_lowrank_workspace_bytes": ("z", "llii"),
     "cf_codes_bytes": ("l", "li"),
     "cf_strerror": ("s", "i"),
     "cf_abi_version": ("i", ""),
@@ -224,3 +227,49 @@ class Slab:
             rc = f(bits, cb + i * cbytes, sb + i * ng * 4, hb + i * n * 4, c * n, s)
             if rc:
                 raise CFError("cf_decompress", rc)
+
+
+def lowrank_workspace_bytes(m: int, n: int, rank: int, batch: int = 1) -> int:
+    nb = lib.cf_lowrank_workspace_bytes(m, n, rank, batch)
+    if nb == 0:
+        raise CFError("cf_lowrank_workspace_bytes", -2)
+    return nb
+
+
+def lowrank_payload(batch: int, m: int, n: int, rank: int, factor_bits: int, device):
+    """Empty payload buffers (u, u_scales, v, v_scales) for `batch` tensors."""
+    if factor_bits == 4:
+        return (torch.empty(batch * m * rank // 2, dtype=torch.uint8, device=device),
+                torch.empty(batch * rank, dtype=torch.float32, device=device),
+                torch.empty(batch * n * rank // 2, dtype=torch.uint8, device=device),
+                torch.empty(batch * rank, dtype=torch.float32, device=device))
+    return (torch.empty(batch * m * rank, dtype=torch.float32, device=device), None,
+            torch.empty(batch * n * rank, dtype=torch.float32, device=device), None)
+
+
+def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
+                     q_state: torch.Tensor, rank: int, iters: int, factor_bits: int = 4,
+                     payload=None, workspace: torch.Tensor | None = None, stream=None):
+    """One low-rank sender step on a (batch, m, n) activation; returns the payload
+    (u, u_scales, v, v_scales).  q_state is (batch, n, rank) fp32, updated in place."""
+    batch, m, n = a.shape
+    if payload is None:
+        payload = lowrank_payload(batch, m, n, rank, factor_bits, a.device)
+    u, us, v, vs = payload
+    need = lowrank_workspace_bytes(m, n, rank, batch)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    _check("cf_lowrank_compress", lib.cf_lowrank_compress(
+        _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err), m, n, rank, iters, factor_bits, batch,
+        _ptr(q_state), _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return u, us, v, vs
+
+
+def lowrank_decompress(factor_bits: int, payload, ahat: torch.Tensor, rank: int, stream=None):
+    """Receiver step on a (batch, m, n) reconstruction: ahat += U^ V^^T."""
+    batch, m, n = ahat.shape
+    u, us, v, vs = payload
+    _check("cf_lowrank_decompress", lib.cf_lowrank_decompress(
+        factor_bits, _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _ptr(ahat), m, n, rank, batch,
+        _stream(stream)))

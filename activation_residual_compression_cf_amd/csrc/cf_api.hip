@@ -144,4 +144,79 @@ int cf_decompress(int bits, const uint8_t* codes, const float* scales, float* ah
                : CF_E_HIP;
 }
 
+size_t cf_lowrank_workspace_bytes(int64_t m, int64_t n, int rank, int batch) {
+    if (m <= 0 || n <= 0 || m % 16 || n % 16 || batch < 1 || rank < 1 || rank > cf::kMaxRank ||
+        rank > m || rank > n || m * n > kMaxNumel / batch)
+        return 0;
+    size_t bytes = 0;
+    cf::carve_lowrank_workspace(nullptr, m, n, rank, batch, &bytes);
+    return bytes;
+}
+
+int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,
+                        int rank, int iters, int factor_bits, int batch, float* q_state, void* u,
+                        float* u_scales, void* v, float* v_scales, void* workspace, size_t ws_bytes,
+                        void* stream) {
+    if (a_dtype != CF_BF16 && a_dtype != CF_F32) return CF_E_ARG;
+    if (factor_bits != 4 && factor_bits != 32) return CF_E_ARG;
+    if (iters < 1 || iters > 64) return CF_E_ARG;
+    if (!a || !ahat || !err || !q_state || !u || !v || !workspace) return CF_E_NULL;
+    if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
+    const size_t need = cf_lowrank_workspace_bytes(m, n, rank, batch);
+    if (need == 0 || (factor_bits == 4 && (rank & 1))) return CF_E_SHAPE;
+    if (!aligned16(a) || !aligned16(ahat) || !aligned16(err) || !aligned4(q_state) ||
+        (factor_bits == 32 && (!aligned4(u) || !aligned4(v))) || (u_scales && !aligned4(u_scales)) ||
+        (v_scales && !aligned4(v_scales)) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return CF_E_ALIGN;
+    if (ws_bytes < need) return CF_E_WORKSPACE;
+    const int64_t numel = m * n * batch;
+    const int64_t fsz = factor_bits == 4 ? 1 : 8;  // factor bytes per (row, rank) pair, times 2
+    const Range r[8] = {range_of(a, act_bytes(a_dtype, numel)),
+                        range_of(ahat, numel * 4),
+                        range_of(err, numel * 4),
+                        range_of(q_state, int64_t(batch) * n * rank * 4),
+                        range_of(u, int64_t(batch) * m * rank * fsz / 2),
+                        range_of(v, int64_t(batch) * n * rank * fsz / 2),
+                        range_of(u_scales, factor_bits == 4 ? int64_t(batch) * rank * 4 : 0),
+                        range_of(v_scales, factor_bits == 4 ? int64_t(batch) * rank * 4 : 0)};
+    const bool out[8] = {false, true, true, true, true, true, factor_bits == 4, factor_bits == 4};
+    if (any_alias(r, out)) return CF_E_ALIAS;
+    const Range wsr = range_of(workspace, static_cast<int64_t>(need));
+    for (const Range& x : r)
+        if (x.hi > x.lo && overlap(x, wsr)) return CF_E_ALIAS;
+    if (int rc = check_device()) return rc;
+    return cf::launch_lowrank_compress(a_dtype, a, ahat, err, m, n, rank, iters, factor_bits, batch,
+                                       q_state, u, u_scales, v, v_scales, workspace,
+                                       static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
+int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
+                          const float* v_scales, float* ahat, int64_t m, int64_t n, int rank,
+                          int batch, void* stream) {
+    if (factor_bits != 4 && factor_bits != 32) return CF_E_ARG;
+    if (!u || !v || !ahat) return CF_E_NULL;
+    if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
+    if (cf_lowrank_workspace_bytes(m, n, rank, batch) == 0 || (factor_bits == 4 && (rank & 1)))
+        return CF_E_SHAPE;
+    if (!aligned16(ahat) || (factor_bits == 32 && (!aligned4(u) || !aligned4(v))) ||
+        (u_scales && !aligned4(u_scales)) || (v_scales && !aligned4(v_scales)))
+        return CF_E_ALIGN;
+    const int64_t numel = m * n * batch;
+    const int64_t fsz = factor_bits == 4 ? 1 : 8;
+    const Range r[5] = {range_of(ahat, numel * 4),
+                        range_of(u, int64_t(batch) * m * rank * fsz / 2),
+                        range_of(v, int64_t(batch) * n * rank * fsz / 2),
+                        range_of(u_scales, factor_bits == 4 ? int64_t(batch) * rank * 4 : 0),
+                        range_of(v_scales, factor_bits == 4 ? int64_t(batch) * rank * 4 : 0)};
+    const bool out[5] = {true, false, false, false, false};
+    if (any_alias(r, out)) return CF_E_ALIAS;
+    if (int rc = check_device()) return rc;
+    return cf::launch_lowrank_decompress(factor_bits, u, u_scales, v, v_scales, ahat, m, n, rank, batch,
+                                         static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
 }  // extern "C"

@@ -17,4 +17,27 @@ hipError_t launch_compress(int bits, int a_dtype, const void* a, float* ahat, fl
 hipError_t launch_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat,
                              int64_t numel, hipStream_t stream);
 
+// Low-rank workspace regions (carved from one caller buffer).
+struct LowrankWorkspace {
+    float* r;      // batch x m x n residual
+    float* qt;     // batch x kp x n, Q transposed (rank padded to a multiple of 16)
+    float* ypart;  // batch x segments x m x kp projection partials
+    float* p;      // batch x m x kp orthonormal factor
+    int* alive;    // batch x kp rank-guard flags
+};
+
+// Largest rank the low-rank kernels accept.
+constexpr int kMaxRank = 64;
+
+// Fills the region pointers for `base` (may be null) and the total size in *bytes.
+LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch,
+                                         size_t* bytes);
+hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m,
+                                   int64_t n, int rank, int iters, int factor_bits, int64_t batch,
+                                   float* q_state, void* u, float* u_scales, void* v, float* v_scales,
+                                   void* workspace, hipStream_t stream);
+hipError_t launch_lowrank_decompress(int factor_bits, const void* u, const float* u_scales,
+                                     const void* v, const float* v_scales, float* ahat, int64_t m,
+                                     int64_t n, int rank, int64_t batch, hipStream_t stream);
+
 }  // namespace cf

@@ -102,6 +102,54 @@ int cf_compress(int bits, int a_dtype, const void* a, float* ahat, float* err, u
 int cf_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat, int64_t numel,
                   void* stream);
 
+/*
+ * Sender step, Compact-Lowrank (Approach: low-rank compression of the residual
+ * with INT4 quantization of the factors; Key results: rank 32 with INT4 factors
+ * gives about 100x; measured-effects table: 2 vs 10 subspace iterations;
+ * Experimental setup, "Builds on": PowerSGD-style subspace iteration).
+ * `batch` tensors of m x n (row-major) laid out back to back.  Per tensor:
+ *   r = a - ahat;  Q = q_state;
+ *   repeat `iters` times:  Y = r Q;  P = orth(Y);  Q = r^T P
+ *     orth: thin QR factor with diag(R) >= 0; a rank-deficient column (|R_jj| <=
+ *     1e-5 ||Y||_F) gives a zero column of P;
+ *   factor_bits 4:  U = int4(P), V = int4(Q): per column j, s_j = max|x| / 7,
+ *     code = rint(x / s_j) clamped to [-7, 7] (0 when s_j = 0), two's-complement
+ *     nibbles, row-major rows x rank, low nibble first;  U^ = code * s_j;
+ *   factor_bits 32: U = P, V = Q as fp32 row-major (rows x rank); scales unused;
+ *   ahat = ahat + U^ V^^T;   err = a - ahat;
+ *   q_state = Q (a column zeroed by the rank guard keeps its previous value).
+ * Buffers (all device memory):
+ *   a: batch*m*n (a_dtype), in; ahat: batch*m*n fp32, in/out; err: out;
+ *   q_state: batch*n*rank fp32, in/out (the start basis; a seeded N(0,1) matrix
+ *     before the first compressed step);
+ *   u: batch*m*rank/2 bytes (4) or batch*m*rank fp32 (32), out;
+ *   v: batch*n*rank/2 bytes (4) or batch*n*rank fp32 (32), out;
+ *   u_scales, v_scales: batch*rank fp32, out (may be NULL when factor_bits = 32);
+ *   workspace: ws_bytes >= cf_lowrank_workspace_bytes(m, n, rank, batch), 256-byte
+ *     aligned; scratch, its contents are not preserved between calls.
+ * Limits: m and n positive multiples of 16; 1 <= rank <= min(m, n, 64); rank even
+ *   when factor_bits = 4; 1 <= iters <= 64; batch >= 1.  a, ahat, err 16-byte
+ *   aligned; the other pointers 4-byte aligned.
+ * Arithmetic is fp32 (fp64 inside orth); results are deterministic.
+ */
+int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,
+                        int rank, int iters, int factor_bits, int batch, float* q_state, void* u,
+                        float* u_scales, void* v, float* v_scales, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * Receiver step, Compact-Lowrank: ahat = ahat + U^ V^^T for `batch` tensors, with
+ * the sender's dequantization and the sender's reconstruction kernel, so the
+ * receiver's ahat equals the sender's bit for bit.  Buffers and limits as in
+ * cf_lowrank_compress; u, u_scales, v, v_scales in; ahat in/out.
+ */
+int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
+                          const float* v_scales, float* ahat, int64_t m, int64_t n, int rank,
+                          int batch, void* stream);
+
+/* Workspace bytes cf_lowrank_compress needs (0 for arguments outside the limits). */
+size_t cf_lowrank_workspace_bytes(int64_t m, int64_t n, int rank, int batch);
+
 /* Bytes of packed codes for numel elements at `bits` per element (numel*bits/8),
  * or a negative status for invalid arguments. */
 int64_t cf_codes_bytes(int64_t numel, int bits);

@@ -114,3 +114,51 @@ def test_init_and_decompress_validation(L):
     assert L.cf_decompress(1, P(0x10000), P(0x20000), P(0x30000), 129, None) == CF_E_SHAPE
     assert L.cf_decompress(2, P(0x10000), P(0x20000), P(0x20000), 128, None) == CF_E_ALIAS
     assert L.cf_decompress(2, P(0x10000), P(0x20000), P(0x30000), 128, None) == CF_E_DEVICE
+
+
+def test_lowrank_validation(L):
+    L.cf_lowrank_workspace_bytes.restype = ctypes.c_size_t
+    L.cf_lowrank_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    assert L.cf_lowrank_workspace_bytes(1024, 3072, 32, 114) > 114 * 1024 * 3072 * 4
+    assert L.cf_lowrank_workspace_bytes(1000, 3072, 32, 1) == 0   # m not a multiple of 16
+    assert L.cf_lowrank_workspace_bytes(1024, 3072, 65, 1) == 0   # rank above 64
+    assert L.cf_lowrank_workspace_bytes(32, 64, 48, 1) == 0       # rank above min(m, n)
+    L.cf_lowrank_compress.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 3 +
+                                      [ctypes.c_int64] * 2 + [ctypes.c_int] * 4 +
+                                      [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
+    ws = L.cf_lowrank_workspace_bytes(64, 128, 8, 1)
+
+    def call(dt=0, a=0x100000, ah=0x200000, e=0x300000, m=64, n=128, k=8, it=2, fb=4, b=1,
+             q=0x400000, u=0x500000, us=0x600000, v=0x700000, vs=0x800000, w=0x1000000, wsb=ws):
+        P_ = lambda x: P(x) if x else None
+        return L.cf_lowrank_compress(dt, P_(a), P_(ah), P_(e), m, n, k, it, fb, b, P_(q), P_(u),
+                                     P_(us), P_(v), P_(vs), P_(w), wsb, None)
+
+    assert call(fb=8) == CF_E_ARG
+    assert call(it=0) == CF_E_ARG
+    assert call(it=65) == CF_E_ARG
+    assert call(w=0) == CF_E_NULL
+    assert call(us=0) == CF_E_NULL
+    assert call(fb=32, us=0, vs=0) == CF_E_DEVICE     # scales optional with fp32 factors
+    assert call(k=7) == CF_E_SHAPE                   # odd rank with INT4
+    assert call(k=0) == CF_E_SHAPE
+    assert call(m=60) == CF_E_SHAPE
+    assert call(b=0) == CF_E_SHAPE
+    assert call(a=0x100008) == CF_E_ALIGN
+    assert call(w=0x1000010) == CF_E_ALIGN           # workspace is 256-byte aligned
+    assert call(wsb=ws - 1) == CF_E_WORKSPACE
+    assert call(e=0x200000 + 64 * 128 * 4 - 16) == CF_E_ALIAS
+    assert call(w=0x200000) == CF_E_ALIAS
+    assert call() == CF_E_DEVICE
+    L.cf_lowrank_decompress.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 5 +
+                                        [ctypes.c_int64] * 2 + [ctypes.c_int] * 2 + [ctypes.c_void_p])
+    assert L.cf_lowrank_decompress(5, P(0x500000), P(0x600000), P(0x700000), P(0x800000),
+                                   P(0x200000), 64, 128, 8, 1, None) == CF_E_ARG
+    assert L.cf_lowrank_decompress(4, P(0x500000), None, P(0x700000), P(0x800000),
+                                   P(0x200000), 64, 128, 8, 1, None) == CF_E_NULL
+    assert L.cf_lowrank_decompress(4, P(0x500000), P(0x600000), P(0x700000), P(0x800000),
+                                   P(0x200000), 64, 100, 8, 1, None) == CF_E_SHAPE
+    assert L.cf_lowrank_decompress(4, P(0x500000), P(0x600000), P(0x700000), P(0x800000),
+                                   P(0x500000), 64, 128, 8, 1, None) == CF_E_ALIAS
+    assert L.cf_lowrank_decompress(4, P(0x500000), P(0x600000), P(0x700000), P(0x800000),
+                                   P(0x200000), 64, 128, 8, 1, None) == CF_E_DEVICE

@@ -1,0 +1,255 @@
+"""GPU parity of the low-rank path (cf_lowrank_compress / cf_lowrank_decompress)
+against the CPU oracle, through the C ABI.
+
+The factors P and Q of a subspace iteration are unique only up to rounding (the GPU
+computes in fp32 with an fp64 Cholesky QR, the oracle in fp64 with Householder QR), and
+one INT4 code can flip where x / s lands on a rounding tie, so the comparisons are:
+  * per step from a shared state: the oracle is given the GPU's Ahat and q_state
+    before the step, and the reconstructed residual R = Ahat_new - Ahat_old must agree
+    to 1e-3 relative Frobenius error (2e-4 with fp32 factors);
+  * stage-isolated INT4: the oracle's quantizer applied to the GPU's own fp32 factors
+    gives the GPU's INT4 codes and scales bit for bit;
+  * properties on every element: err == a - Ahat, receiver == sender bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from gpu_util import host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cf():
+    from activation_residual_compression_cf_amd import cf as _cf
+
+    return _cf
+
+
+@pytest.fixture(scope="module")
+def dev(cf):
+    return cf.require_device()
+
+
+@pytest.fixture(scope="module")
+def O():
+    return oracle.default()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def start_bases(seed, slots, n, rank):
+    return np.stack([gen.start_basis(seed, s, n, rank) for s in range(slots)])
+
+
+def check_step(cf, dev, O, A_prev_host, A_host, ahat_d, err_d, qs_d, rank, iters, fb, samples,
+               tol):
+    """Run one GPU step and compare sampled tensors with the oracle from the shared state."""
+    batch, m, n = A_host.shape
+    ah_before = {s: host(ahat_d[s]).copy() for s in samples}
+    qs_before = {s: host(qs_d[s]).copy() for s in samples}
+    a_d = to_dev(A_host, dev)
+    payload = cf.lowrank_compress(a_d, ahat_d, err_d, qs_d, rank, iters, fb)
+    torch.cuda.synchronize()
+    a32 = a_d.float()
+    assert torch.equal(err_d, a32 - ahat_d), "err != a - ahat"
+    for s in samples:
+        ah_o = ah_before[s].copy()
+        er_o = np.zeros_like(ah_o)
+        q_o = qs_before[s].copy()
+        O.lowrank_compress(np.ascontiguousarray(A_host[s]), ah_o, er_o, q_o, rank, iters, fb)
+        r_gpu = host(ahat_d[s]).astype(np.float64) - ah_before[s]
+        r_orc = ah_o.astype(np.float64) - ah_before[s]
+        e = rel(r_gpu, r_orc)
+        say(f"  slot {s}: rel(R_gpu, R_oracle) = {e:.2e}, rel(q_state) = {rel(host(qs_d[s]), q_o):.2e}")
+        assert e <= tol, f"slot {s}: reconstruction differs by {e:.3e}"
+    return payload
+
+
+@pytest.mark.parametrize("rank,iters,fb,dtype", [(8, 2, 4, "bf16"), (16, 1, 4, "f32"),
+                                                 (32, 2, 4, "bf16"), (32, 3, 32, "bf16"),
+                                                 (48, 2, 4, "bf16"), (64, 1, 32, "f32"),
+                                                 (8, 10, 4, "bf16")])
+def test_step_parity_small(cf, dev, O, rank, iters, fb, dtype):
+    """3 tensors of 128 x 320 (several tiles, a partial column segment), 3 steps."""
+    wl = gen.Workload("lr", 128, 320, 3, 4, dtype, dtype == "bf16")
+    say(f"lowrank small: rank={rank} iters={iters} fb={fb} dtype={dtype}")
+    tr = gen.Trajectory(wl, 1)
+    A0 = tr.next()
+    a0 = to_dev(A0, dev)
+    ahat = torch.empty((3, 128, 320), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(a0, ahat, err)
+    qs = torch.from_numpy(start_bases(1, 3, 320, rank)).to(dev)
+    prev = A0
+    for t in range(1, 4):
+        A = tr.next()
+        check_step(cf, dev, O, prev, A, ahat, err, qs, rank, iters, fb, samples=[0, 1, 2],
+                   tol=1e-3 if fb == 4 else 2e-4)
+        prev = A
+
+
+def test_int4_stage_isolated(cf, dev, O):
+    """The INT4 codes and scales equal the oracle's quantizer on the GPU's fp32 factors."""
+    wl = gen.Workload("lr", 256, 768, 2, 2, "bf16", True)
+    tr = gen.Trajectory(wl, 2)
+    A0, A1 = tr.next(), tr.next()
+    for rank in (8, 32):
+        say(f"int4 stage isolated rank={rank}")
+        outs = {}
+        for fb in (32, 4):
+            a0 = to_dev(A0, dev)
+            ahat = torch.empty((2, 256, 768), dtype=torch.float32, device=dev)
+            err = torch.empty_like(ahat)
+            cf.init_state(a0, ahat, err)
+            qs = torch.from_numpy(start_bases(2, 2, 768, rank)).to(dev)
+            outs[fb] = cf.lowrank_compress(to_dev(A1, dev), ahat, err, qs, rank, 2, fb)
+        torch.cuda.synchronize()
+        u32, _, v32, _ = outs[32]
+        u4, us4, v4, vs4 = outs[4]
+        for b in range(2):
+            P = host(u32).reshape(2, 256, rank)[b]
+            Q = host(v32).reshape(2, 768, rank)[b]
+            pu, su = O.int4_quantize(P)
+            pv, sv = O.int4_quantize(Q)
+            assert np.array_equal(host(u4).reshape(2, -1)[b], pu)
+            assert np.array_equal(host(us4).reshape(2, rank)[b], su)
+            assert np.array_equal(host(v4).reshape(2, -1)[b], pv)
+            assert np.array_equal(host(vs4).reshape(2, rank)[b], sv)
+
+
+def test_full_rank_reproduces_residual(cf, dev):
+    """rank = min(m, n) with fp32 factors reproduces r (1e-5 relative)."""
+    for m, n in ((48, 64), (64, 32)):
+        say(f"full rank {m}x{n}")
+        k = min(m, n)
+        rng = np.random.default_rng(3)
+        a = rng.standard_normal((1, m, n)).astype(np.float32)
+        ah0 = (0.5 * rng.standard_normal((1, m, n))).astype(np.float32)
+        r = (a - ah0).astype(np.float64)
+        ahat = to_dev(ah0, dev)
+        err = torch.empty_like(ahat)
+        qs = to_dev(rng.standard_normal((1, n, k)).astype(np.float32), dev)
+        cf.lowrank_compress(to_dev(a, dev), ahat, err, qs, k, 1, 32)
+        torch.cuda.synchronize()
+        rhat = host(ahat).astype(np.float64) - ah0
+        assert rel(rhat, r) <= 1e-5, rel(rhat, r)
+
+
+def test_planted_rank_and_zero_residual(cf, dev):
+    rng = np.random.default_rng(4)
+    m, n, k0, k = 96, 160, 3, 8
+    r = (rng.integers(-3, 4, (m, k0)) @ rng.integers(-3, 4, (k0, n))).astype(np.float32)[None]
+    say("planted rank")
+    ahat = torch.zeros((1, m, n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    q0 = rng.standard_normal((1, n, k)).astype(np.float32)
+    qs = to_dev(q0, dev)
+    u, _, v, _ = cf.lowrank_compress(to_dev(r, dev), ahat, err, qs, k, 1, 32)
+    torch.cuda.synchronize()
+    assert rel(host(ahat), r) <= 1e-5
+    U = host(u).reshape(m, k)
+    assert np.count_nonzero(np.abs(U).sum(0)) == k0, "rank-deficient columns are zero"
+    dead = np.abs(U).sum(0) == 0
+    assert np.array_equal(host(qs)[0][:, dead], q0[0][:, dead]), "dead columns keep their start"
+    say("zero residual")
+    a = rng.standard_normal((2, m, n)).astype(np.float32)
+    ahat = to_dev(a, dev)
+    err = torch.full_like(ahat, 5.0)
+    q0 = rng.standard_normal((2, n, k)).astype(np.float32)
+    qs = to_dev(q0, dev)
+    u, us, v, vs = cf.lowrank_compress(to_dev(a, dev), ahat, err, qs, k, 2, 4)
+    torch.cuda.synchronize()
+    assert not host(u).any() and not host(v).any() and not host(us).any() and not host(vs).any()
+    assert np.array_equal(host(ahat), a) and not host(err).any()
+    assert np.array_equal(host(qs), q0)
+
+
+@pytest.mark.parametrize("fb", [4, 32])
+def test_receiver_matches_sender(cf, dev, fb):
+    wl = gen.Workload("lr", 192, 512, 2, 4, "bf16", True)
+    tr = gen.Trajectory(wl, 5)
+    a0 = to_dev(tr.next(), dev)
+    ahat = torch.empty((2, 192, 512), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(a0, ahat, err)
+    rx = torch.empty_like(ahat)
+    cf.init_state(a0, rx)
+    qs = torch.from_numpy(start_bases(5, 2, 512, 16)).to(dev)
+    for t in range(1, 4):
+        say(f"receiver fb={fb} step {t}")
+        payload = cf.lowrank_compress(to_dev(tr.next(), dev), ahat, err, qs, 16, 2, fb)
+        cf.lowrank_decompress(fb, payload, rx, 16)
+        torch.cuda.synchronize()
+        assert torch.equal(rx, ahat)
+
+
+@pytest.mark.parametrize("rank,iters", [(32, 2), (8, 10)])
+def test_flux_shape(cf, dev, O, rank, iters):
+    """114 x (1024 x 3072) bf16 per call, INT4 factors; two compressed steps; oracle on
+    sampled tensors from the shared state; every element checked for err == a - Ahat."""
+    wl = gen.WORKLOADS["flux"]
+    say(f"lowrank FLUX shape rank={rank} iters={iters}")
+    tr = gen.Trajectory(wl, 0)
+    A0 = tr.next()
+    a0 = to_dev(A0, dev)
+    ahat = torch.empty((wl.slots, wl.m, wl.n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(a0, ahat, err)
+    del a0
+    qs = torch.from_numpy(start_bases(0, wl.slots, wl.n, rank)).to(dev)
+    prev = A0
+    for t in (1, 2):
+        A = tr.next()
+        check_step(cf, dev, O, prev, A, ahat, err, qs, rank, iters, 4, samples=[0, 113], tol=1e-3)
+        prev = A
+
+
+def test_deterministic(cf, dev):
+    wl = gen.Workload("lr", 256, 768, 3, 2, "bf16", True)
+    tr = gen.Trajectory(wl, 6)
+    A0, A1 = tr.next(), tr.next()
+    res = []
+    for _ in range(2):
+        say("lowrank determinism run")
+        ahat = torch.empty((3, 256, 768), dtype=torch.float32, device=dev)
+        err = torch.empty_like(ahat)
+        cf.init_state(to_dev(A0, dev), ahat, err)
+        qs = torch.from_numpy(start_bases(6, 3, 768, 32)).to(dev)
+        pay = cf.lowrank_compress(to_dev(A1, dev), ahat, err, qs, 32, 2, 4)
+        torch.cuda.synchronize()
+        res.append([x.clone() for x in (ahat, err, qs, *pay)])
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
+
+
+def test_failed_call_writes_nothing(cf, dev):
+    m, n, k = 64, 128, 8
+    a = torch.randn((1, m, n), device=dev)
+    ahat = torch.zeros((1, m, n), device=dev)
+    err = torch.full((1, m, n), 3.0, device=dev)
+    qs = torch.randn((1, n, k), device=dev)
+    snap = [x.clone() for x in (ahat, err, qs)]
+    small_ws = torch.empty(1024, dtype=torch.uint8, device=dev)
+    with pytest.raises(cf.CFError) as ei:
+        cf.lowrank_compress(a, ahat, err, qs, k, 2, 4, workspace=small_ws)
+    assert ei.value.status == -6
+    with pytest.raises(cf.CFError) as ei:
+        cf.lowrank_compress(a, ahat, err, qs, 7, 2, 4)  # odd rank with INT4
+    assert ei.value.status == -2
+    with pytest.raises(cf.CFError):
+        cf.lowrank_compress(a[:, :, :120].contiguous(), ahat[:, :, :120].contiguous(),
+                            err[:, :, :120].contiguous(), qs[:, :120].contiguous(), k, 2, 4)
+    torch.cuda.synchronize()
+    for x, y in zip((ahat, err, qs), snap):
+        assert torch.equal(x, y)
