@@ -165,7 +165,7 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
     const size_t need = cf_lowrank_workspace_bytes(m, n, rank, batch);
     if (need == 0 || (factor_bits == 4 && (rank & 1))) return CF_E_SHAPE;
     if (!aligned16(a) || !aligned16(ahat) || !aligned16(err) || !aligned4(q_state) ||
-        (factor_bits == 32 && (!aligned4(u) || !aligned4(v))) || (u_scales && !aligned4(u_scales)) ||
+        !aligned4(u) || !aligned4(v) || (u_scales && !aligned4(u_scales)) ||
         (v_scales && !aligned4(v_scales)) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return CF_E_ALIGN;
     if (ws_bytes < need) return CF_E_WORKSPACE;
@@ -200,8 +200,8 @@ int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales,
     if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
     if (cf_lowrank_workspace_bytes(m, n, rank, batch) == 0 || (factor_bits == 4 && (rank & 1)))
         return CF_E_SHAPE;
-    if (!aligned16(ahat) || (factor_bits == 32 && (!aligned4(u) || !aligned4(v))) ||
-        (u_scales && !aligned4(u_scales)) || (v_scales && !aligned4(v_scales)))
+    if (!aligned16(ahat) || !aligned4(u) || !aligned4(v) || (u_scales && !aligned4(u_scales)) ||
+        (v_scales && !aligned4(v_scales)))
         return CF_E_ALIGN;
     const int64_t numel = m * n * batch;
     const int64_t fsz = factor_bits == 4 ? 1 : 8;

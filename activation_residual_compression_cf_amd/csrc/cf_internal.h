@@ -24,6 +24,9 @@ struct LowrankWorkspace {
     float* ypart;  // batch x segments x m x kp projection partials
     float* p;      // batch x m x kp orthonormal factor
     int* alive;    // batch x kp rank-guard flags
+    double* gpart; // batch x row blocks x kp x kp Gram partials
+    double* xinv;  // batch x kp x kp inverse Cholesky factor
+    float* cmax;   // batch x row blocks x kp column maxima of the factors
 };
 
 // Largest rank the low-rank kernels accept.

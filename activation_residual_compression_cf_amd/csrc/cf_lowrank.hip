@@ -43,10 +43,10 @@ namespace {
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef unsigned vu2 __attribute__((ext_vector_type(2)));
 
-constexpr int kSegCols = 768;   // columns per projection segment
+constexpr int kSegCols = 512;   // columns per projection segment
 constexpr int kProjRows = 256;  // rows per projection workgroup (4 waves x 64)
-constexpr int kBackCols = 128;  // columns per back-projection workgroup
-constexpr int kRecRows = 64;    // reconstruction workgroup: 64 rows x 256 columns
+constexpr int kBackCols = 256;  // columns per back-projection workgroup
+constexpr int kRecRows = 128;   // reconstruction workgroup: 128 rows x 256 columns
 constexpr int kRecCols = 256;
 
 __device__ __forceinline__ vf4 mfma4(float a, float b, vf4 c) {
@@ -65,6 +65,29 @@ __device__ __forceinline__ vf4 act4(const uint16_t* a, int64_t off) {
                __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
 }
 __device__ __forceinline__ vf4 act4(const float* a, int64_t off) { return ld4_nt(a + off); }
+
+// Activation loads kept raw until use, so a prefetch does not wait for its data.
+template <typename ActT>
+struct RawAct;
+template <>
+struct RawAct<uint16_t> {
+    using T = vu2;
+    static __device__ __forceinline__ vu2 load(const uint16_t* a, int64_t off) {
+        return __builtin_nontemporal_load(reinterpret_cast<const vu2*>(a + off));
+    }
+    static __device__ __forceinline__ vu2 zero() { return vu2{0u, 0u}; }
+    static __device__ __forceinline__ vf4 cvt(vu2 w) {
+        return vf4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+    }
+};
+template <>
+struct RawAct<float> {
+    using T = vf4;
+    static __device__ __forceinline__ vf4 load(const float* a, int64_t off) { return ld4_nt(a + off); }
+    static __device__ __forceinline__ vf4 zero() { return vf4{0.f, 0.f, 0.f, 0.f}; }
+    static __device__ __forceinline__ vf4 cvt(vf4 w) { return w; }
+};
 
 // The hardware hands workgroup w to XCD w % 8.  Renumber so that each XCD walks a
 // contiguous range of logical workgroups (consecutive tiles of the same tensors),
@@ -86,201 +109,283 @@ __global__ __launch_bounds__(256) void k_lr_prep(const float* __restrict__ q_sta
 }
 
 // ------------------------------------------------------------- project ----
-// Workgroup: 4 waves, 64 rows each (4 M-tiles of 16), one column segment.
-// Ypart[b][s][row][kp] = sum over the segment's columns of r[row][c] Q[c][kk].
+// Workgroup: 4 waves over columns [c0, c0 + 512) and rows [r0, r0 + 256), in
+// stages of 16 rows.  Wave w owns columns c0 + 128 w .. + 127 and keeps the matching
+// Q^T float4 operands (8 column groups x KT tiles) in registers for the whole
+// kernel.  Per stage the 16 x 512 slab of r is formed (first pass: a - Ahat, also
+// stored to the workspace) or read, one instruction per 256 consecutive columns
+// of a row, and staged in LDS; each wave multiplies its 128 columns (MFMA, a lane's
+// float4 of r supplying 4 k-slices), the four partial Y tiles are summed in LDS in
+// wave order, and the 16 x kp result goes to Ypart[b][segment][row][kp].
 template <bool FIRST, typename ActT, int KT>
 __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, const float* __restrict__ ahat,
                                                      float* __restrict__ r, const float* __restrict__ qt,
                                                      float* __restrict__ ypart, int64_t m, int64_t n,
                                                      int64_t batch, int64_t nseg, int64_t total) {
     constexpr int kp = 16 * KT;
+    constexpr int kStage = 16;
+    __shared__ float slab[kStage][kSegCols + 4];
+    __shared__ float red[4][kStage][kp + 1];
     const int64_t lw = xcd_remap(blockIdx.x, total);
     const int64_t rblocks = (m + kProjRows - 1) / kProjRows;
-    if (lw >= batch * rblocks * nseg) return;  // padding workgroups of the remap
+    if (lw >= batch * rblocks * nseg) return;  // uniform per workgroup
     const int64_t b = lw / (rblocks * nseg);
     const int64_t rb = (lw / nseg) % rblocks;
-    const int64_t s = lw % nseg;
+    const int64_t sgi = lw % nseg;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int64_t row0 = rb * kProjRows + wave * 64;
-    const int64_t c_begin = s * kSegCols;
-    const int64_t c_end = c_begin + kSegCols < n ? c_begin + kSegCols : n;
+    const int64_t c0 = sgi * kSegCols;
     const int64_t mn = m * n;
 
-    bool mt_ok[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) mt_ok[mt] = row0 + 16 * mt < m;
-
-    vf4 acc[4][KT];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int t = 0; t < KT; ++t) acc[mt][t] = vf4{0.f, 0.f, 0.f, 0.f};
-
+    // Q^T operands: column group g covers columns c0 + 128 w + 16 g .. + 15;
+    // lane: Q^T[16 t + li][c0 + 128 w + 16 g + 4 lg .. + 3].
     const float* qtb = qt + b * kp * n;
-    for (int64_t c = c_begin; c < c_end; c += 16) {
-        const int64_t col = c + 4 * lg;
-        vf4 rv[4];
+    vf4 qv[8][KT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int64_t off = b * mn + (row0 + 16 * mt + li) * n + col;
-            if (mt_ok[mt]) {
-                if constexpr (FIRST) {
-                    rv[mt] = act4(a, off) - ld4_nt(ahat + off);
-                    st4_nt(r + off, rv[mt]);
-                } else {
-                    rv[mt] = ld4(r + off);
-                }
-            } else {
-                rv[mt] = vf4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        vf4 qv[KT];
+    for (int g = 0; g < 8; ++g) {
+        const int64_t col = c0 + 128 * wave + 16 * g + 4 * lg;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) qv[t] = ld4(qtb + (16 * t + li) * n + col);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int t = 0; t < KT; ++t) acc[mt][t] = mfma4(rv[mt][i], qv[t][i], acc[mt][t]);
+        for (int t = 0; t < KT; ++t)
+            qv[g][t] = col < n ? ld4(qtb + (16 * t + li) * n + col) : vf4{0.f, 0.f, 0.f, 0.f};
     }
-    // acc[mt][t] lane: rows row0 + 16 mt + 4 lg + v, column 16 t + li
-    float* yp = ypart + ((b * nseg + s) * m) * kp;
+
+    const int64_t rend = (rb + 1) * kProjRows < m ? (rb + 1) * kProjRows : m;
+    // staging: wave w forms rows sr + 4 w + q; lane l columns c0 + 256 h + 4 l
+    using RA = RawAct<ActT>;
+    typename RA::T pa[4][2];
+    vf4 ph[4][2];
+    auto fetch = [&](int64_t sr) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        if (!mt_ok[mt]) continue;
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t col = c0 + 256 * h + 4 * lane;
+                const int64_t off = b * mn + (sr + 4 * wave + q) * n + col;
+                const bool ok = col < n;
+                if constexpr (FIRST) {
+                    pa[q][h] = ok ? RA::load(a, off) : RA::zero();
+                    ph[q][h] = ok ? ld4_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    ph[q][h] = ok ? ld4(r + off) : vf4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+    };
+    int64_t sr = rb * kProjRows;
+    if (sr < rend) fetch(sr);
+    for (; sr < rend; sr += kStage) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int rr = 4 * wave + q;
+                const int cc = 256 * h + 4 * lane;
+                vf4 x = ph[q][h];
+                if constexpr (FIRST) {
+                    x = RA::cvt(pa[q][h]) - x;
+                    if (c0 + cc < n) st4_nt(r + b * mn + (sr + rr) * n + c0 + cc, x);
+                }
+                *reinterpret_cast<vf4*>(&slab[rr][cc]) = x;
+            }
+        __syncthreads();
+        if (sr + kStage < rend) fetch(sr + kStage);  // next stage's loads overlap the MFMAs
+        vf4 acc[KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) acc[t] = vf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const vf4 rv = *reinterpret_cast<const vf4*>(&slab[li][128 * wave + 16 * g + 4 * lg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < KT; ++t) acc[t] = mfma4(rv[i], qv[g][t][i], acc[t]);
+        }
+        // acc[t] lane: rows 4 lg + v of the stage, Y column 16 t + li
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) yp[(row0 + 16 * mt + 4 * lg + v) * kp + 16 * t + li] = acc[mt][t][v];
+            for (int v = 0; v < 4; ++v) red[wave][4 * lg + v][16 * t + li] = acc[t][v];
+        __syncthreads();
+        float* yp = ypart + ((b * nseg + sgi) * m + sr) * kp;
+        for (int e = threadIdx.x; e < kStage * kp; e += 256) {
+            const int rr = e / kp, kk = e % kp;
+            yp[rr * kp + kk] = ((red[0][rr][kk] + red[1][rr][kk]) + red[2][rr][kk]) + red[3][rr][kk];
+        }
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------- orth ----
-// One workgroup (256 threads) per tensor.  Y rows are staged through LDS as fp64
-// in chunks of 16 rows; thread (ti, tj) of a 16 x 16 grid owns the KT x KT block of
-// the Gram matrix G = Y^T Y at rows ti*KT.., columns tj*KT.. .  The Cholesky factor
-// L overwrites G's lower triangle; Li = L^-1; P = Y (L^T)^-1 = Y Li^T.
+// orth(Y) in three launches:
+//   k_lr_gram   (batch x row blocks) Y = sum of the segment partials in segment
+//               order (fp32, written to `p` for the solve), and the fp64 Gram
+//               contribution Y_blk^T Y_blk of the block's rows;
+//   k_lr_chol   (one workgroup per tensor) G = sum of the block Grams in block
+//               order; right-looking Cholesky G = L L^T in LDS with the rank guard
+//               (pivot <= 1e-10 trace(G) -> dead column); X = L^-1;
+//   k_lr_solve  (batch x row blocks) P[row] = Y[row] X^T in fp64, in place over Y.
 template <int KT>
-__global__ __launch_bounds__(256) void k_lr_orth(const float* __restrict__ ypart, float* __restrict__ p,
-                                                  int* __restrict__ alive, int64_t m, int64_t nseg, int k) {
-    constexpr int kp = 16 * KT;
-    constexpr int CH = 16;
-    __shared__ double ys[CH][kp + 1];
-    __shared__ double G[kp][kp + 1];
-    __shared__ double Li[kp][kp + 1];
-    __shared__ int dead[kp];
+struct GramShape {
+    static constexpr int kp = 16 * KT;
+    static constexpr int rows = KT == 1 ? 256 : (KT == 2 ? 128 : 64);  // rows per Gram block
+};
+
+template <int KT>
+__global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart, float* __restrict__ p,
+                                                  double* __restrict__ gpart, int64_t m, int64_t nseg,
+                                                  int64_t batch) {
+    constexpr int kp = GramShape<KT>::kp;
+    constexpr int GR = GramShape<KT>::rows;
+    __shared__ double ys[GR][kp + 1];
+    const int64_t gblocks = (m + GR - 1) / GR;
+    const int64_t b = blockIdx.x / gblocks;
+    const int64_t blk = blockIdx.x % gblocks;
+    const int64_t r0 = blk * GR;
     const int tid = threadIdx.x;
-    const int64_t b = blockIdx.x;
     const float* yb = ypart + b * nseg * m * kp;
+    float* pb = p + b * m * kp;
+    for (int e = tid; e < GR * kp; e += 256) {
+        const int rr = e / kp, kk = e % kp;
+        const int64_t row = r0 + rr;
+        double y = 0.0;
+        if (row < m) {
+            float s = yb[row * kp + kk];
+            for (int64_t q = 1; q < nseg; ++q) s = s + yb[(q * m + row) * kp + kk];
+            pb[row * kp + kk] = s;
+            y = static_cast<double>(s);
+        }
+        ys[rr][kk] = y;
+    }
+    __syncthreads();
     const int ti = tid >> 4, tj = tid & 15;
-
-    // Y[row][kk]: the segment partials summed in segment order (fp32), widened.
-    auto yval = [&](int64_t row, int kk) -> double {
-        float s = yb[row * kp + kk];
-        for (int64_t q = 1; q < nseg; ++q) s = s + yb[(q * m + row) * kp + kk];
-        return static_cast<double>(s);
-    };
-
     double g[KT][KT];
 #pragma unroll
     for (int i = 0; i < KT; ++i)
 #pragma unroll
         for (int j = 0; j < KT; ++j) g[i][j] = 0.0;
-    for (int64_t r0 = 0; r0 < m; r0 += CH) {
-        for (int e = tid; e < CH * kp; e += 256) {
-            const int rr = e / kp, kk = e % kp;
-            ys[rr][kk] = (r0 + rr < m) ? yval(r0 + rr, kk) : 0.0;
-        }
-        __syncthreads();
-        for (int rr = 0; rr < CH; ++rr) {
-            double yi[KT], yj[KT];
+    for (int rr = 0; rr < GR; ++rr) {
+        double yi[KT], yj[KT];
 #pragma unroll
-            for (int i = 0; i < KT; ++i) yi[i] = ys[rr][ti * KT + i];
+        for (int i = 0; i < KT; ++i) yi[i] = ys[rr][ti * KT + i];
 #pragma unroll
-            for (int j = 0; j < KT; ++j) yj[j] = ys[rr][tj * KT + j];
+        for (int j = 0; j < KT; ++j) yj[j] = ys[rr][tj * KT + j];
 #pragma unroll
-            for (int i = 0; i < KT; ++i)
+        for (int i = 0; i < KT; ++i)
 #pragma unroll
-                for (int j = 0; j < KT; ++j) g[i][j] = fma(yi[i], yj[j], g[i][j]);
-        }
-        __syncthreads();
+            for (int j = 0; j < KT; ++j) g[i][j] = fma(yi[i], yj[j], g[i][j]);
     }
+    double* gp = gpart + (b * gblocks + blk) * kp * kp;
 #pragma unroll
     for (int i = 0; i < KT; ++i)
 #pragma unroll
-        for (int j = 0; j < KT; ++j) G[ti * KT + i][tj * KT + j] = g[i][j];
-    __syncthreads();
+        for (int j = 0; j < KT; ++j) gp[(ti * KT + i) * kp + tj * KT + j] = g[i][j];
+}
 
+template <int KT>
+__global__ __launch_bounds__(256) void k_lr_chol(const double* __restrict__ gpart, double* __restrict__ xinv,
+                                                  int* __restrict__ alive, int64_t gblocks, int k) {
+    constexpr int kp = 16 * KT;
+    __shared__ double G[kp][kp + 1];  // Gram, then L in its lower triangle
+    __shared__ double X[kp][kp + 1];  // L^-1
+    __shared__ int dead[kp];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const double* gb = gpart + b * gblocks * kp * kp;
+    for (int e = tid; e < kp * kp; e += 256) {
+        double s = gb[e];
+        for (int64_t q = 1; q < gblocks; ++q) s += gb[q * kp * kp + e];
+        G[e / kp][e % kp] = s;
+        X[e / kp][e % kp] = (e / kp == e % kp) ? 1.0 : 0.0;
+    }
+    __syncthreads();
     double tr = 0.0;
     for (int j = 0; j < kp; ++j) tr += G[j][j];
     const double thresh = 1e-10 * tr;
     __syncthreads();  // every trace read precedes the in-place factorisation
-    // Cholesky, column by column, in place in the lower triangle of G.
     for (int j = 0; j < kp; ++j) {
         if (tid == 0) {
-            double d = G[j][j];
-            for (int q = 0; q < j; ++q) d -= G[j][q] * G[j][q];
+            const double d = G[j][j];
             const bool ok = j < k && d > thresh;
             G[j][j] = ok ? sqrt(d) : 0.0;
             dead[j] = ok ? 0 : 1;
         }
         __syncthreads();
-        const bool ok = dead[j] == 0;
-        for (int i = j + 1 + tid; i < kp; i += 256) {
-            double v = G[i][j];
-            for (int q = 0; q < j; ++q) v -= G[i][q] * G[j][q];
-            G[i][j] = ok ? v / G[j][j] : 0.0;
+        const bool dj = dead[j] != 0;
+        for (int i = j + 1 + tid; i < kp; i += 256) G[i][j] = dj ? 0.0 : G[i][j] / G[j][j];
+        __syncthreads();
+        // trailing update of the lower triangle: G[i][l] -= L[i][j] L[l][j], j < l <= i
+        for (int e = tid; e < kp * kp; e += 256) {
+            const int i = e / kp, l = e % kp;
+            if (l > j && l <= i) G[i][l] -= G[i][j] * G[l][j];
         }
         __syncthreads();
     }
-    // Li = L^-1, column c by thread c (forward substitution; dead rows give 0).
-    if (tid < kp) {
-        const int c = tid;
-        for (int i = 0; i < kp; ++i) {
-            double x = 0.0;
-            if (i >= c && dead[i] == 0) {
-                double v = (i == c) ? 1.0 : 0.0;
-                for (int q = c; q < i; ++q) v -= G[i][q] * Li[q][c];
-                x = v / G[i][i];
-            }
-            Li[i][c] = x;
+    // X = L^-1 by forward elimination on the rows of the identity
+    for (int j = 0; j < kp; ++j) {
+        const bool dj = dead[j] != 0;
+        for (int c = tid; c <= j; c += 256) X[j][c] = dj ? 0.0 : X[j][c] / G[j][j];
+        __syncthreads();
+        for (int e = tid; e < (kp - j - 1) * (j + 1); e += 256) {
+            const int i = j + 1 + e / (j + 1), c = e % (j + 1);
+            X[i][c] -= G[i][j] * X[j][c];
         }
+        __syncthreads();
     }
-    __syncthreads();
+    double* xb = xinv + b * kp * kp;
+    for (int e = tid; e < kp * kp; e += 256) xb[e] = X[e / kp][e % kp];
     if (tid < kp) alive[b * kp + tid] = dead[tid] ? 0 : 1;
+}
 
-    // P[row][j] = sum_{i <= j} Y[row][i] Li[j][i], with Y rows staged in LDS again.
-    float* pb = p + b * m * kp;
-    for (int64_t r0 = 0; r0 < m; r0 += CH) {
-        for (int e = tid; e < CH * kp; e += 256) {
-            const int rr = e / kp, kk = e % kp;
-            ys[rr][kk] = (r0 + rr < m) ? yval(r0 + rr, kk) : 0.0;
-        }
-        __syncthreads();
-        for (int e = tid; e < CH * kp; e += 256) {
-            const int rr = e / kp, j = e % kp;
+// P[row][j] = sum_{i <= j} Y[row][i] X[j][i]; one row per thread, in place.
+template <int KT>
+__global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const double* __restrict__ xinv,
+                                                   int64_t m, int64_t batch) {
+    constexpr int kp = 16 * KT;
+    __shared__ double X[kp][kp + 1];
+    const int64_t rblocks = (m + 255) / 256;
+    const int64_t b = blockIdx.x / rblocks;
+    const int64_t row = (blockIdx.x % rblocks) * 256 + threadIdx.x;
+    const double* xb = xinv + b * kp * kp;
+    for (int e = threadIdx.x; e < kp * kp; e += 256) X[e / kp][e % kp] = xb[e];
+    __syncthreads();
+    if (row >= m) return;
+    float* pr = p + (b * m + row) * kp;
+    double y[kp];
+#pragma unroll
+    for (int i = 0; i < kp; i += 4) {
+        const vf4 v = ld4(pr + i);
+        y[i] = v[0]; y[i + 1] = v[1]; y[i + 2] = v[2]; y[i + 3] = v[3];
+    }
+#pragma unroll
+    for (int j = 0; j < kp; j += 4) {
+        vf4 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
             double acc = 0.0;
-            for (int i = 0; i <= j; ++i) acc = fma(ys[rr][i], Li[j][i], acc);
-            if (r0 + rr < m) pb[(r0 + rr) * kp + j] = static_cast<float>(acc);
+#pragma unroll
+            for (int i = 0; i <= j + jj; ++i) acc = fma(y[i], X[j + jj][i], acc);
+            o[jj] = static_cast<float>(acc);
         }
-        __syncthreads();
+        *reinterpret_cast<vf4*>(pr + j) = o;
     }
 }
 
 // ---------------------------------------------------------- backproject ----
-// Workgroup: 4 waves over the same 128 columns; wave w takes the 4-row steps
-// w, w + 4, w + 8, ...  Lane: rows row + lg, columns c0 + 64 h + 4 li .. + 3.
+// Workgroup: 4 waves over columns [c0, c0 + 256) and every row, in stages of 16
+// rows.  Per stage the 16 x 256 slab of r (one instruction per row) and the 16 x kp
+// block of P are staged in LDS; wave w owns columns c0 + 64 w .. + 63 and
+// accumulates Q^T[kk][col] = sum_rows P[row][kk] r[row][col] with MFMA (4 rows per
+// k-slice; a lane's float4 of r gives 4 column sets).  No cross-wave reduction.
 template <int KT>
 __global__ __launch_bounds__(256) void k_lr_backproject(const float* __restrict__ r, const float* __restrict__ p,
                                                          float* __restrict__ qt, int64_t m, int64_t n,
                                                          int64_t batch, int64_t total) {
     constexpr int kp = 16 * KT;
-    __shared__ float red[kp][kBackCols + 4];
+    constexpr int kStage = 16;
+    __shared__ float slab[kStage][kBackCols + 4];
+    __shared__ float ps[kStage][kp + 1];
     const int64_t cblocks = (n + kBackCols - 1) / kBackCols;
     const int64_t lw = xcd_remap(blockIdx.x, total);
-    if (lw >= batch * cblocks) return;
+    if (lw >= batch * cblocks) return;  // uniform per workgroup
     const int64_t b = lw / cblocks;
     const int64_t c0 = (lw % cblocks) * kBackCols;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -289,132 +394,244 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* __restrict_
     const float* rb = r + b * mn;
     const float* pb = p + b * m * kp;
 
-    bool h_ok[2];
+    vf4 acc[4][KT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) h_ok[h] = c0 + 64 * h + 4 * li < n;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < KT; ++t) acc[i][t] = vf4{0.f, 0.f, 0.f, 0.f};
 
-    vf4 acc[2][4][KT];
+    const int64_t col = c0 + 4 * lane;  // staging column of this lane
+    constexpr int PPT = (kStage * kp + 255) / 256;  // P values staged per thread
+    vf4 rq[4];
+    float pq[PPT];
+    auto fetch = [&](int64_t sr) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+        for (int q = 0; q < 4; ++q)
+            rq[q] = col < n ? ld4(rb + (sr + 4 * wave + q) * n + col) : vf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < PPT; ++j) {
+            const int e = threadIdx.x + 256 * j;
+            pq[j] = e < kStage * kp ? pb[(sr + e / kp) * kp + e % kp] : 0.0f;
+        }
+    };
+    fetch(0);
+    for (int64_t sr = 0; sr < m; sr += kStage) {
 #pragma unroll
-            for (int t = 0; t < KT; ++t) acc[h][i][t] = vf4{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t row = 4 * wave; row < m; row += 16) {
-        const int64_t rr = row + lg;
-        vf4 rv[2];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&slab[4 * wave + q][4 * lane]) = rq[q];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            rv[h] = h_ok[h] ? ld4(rb + rr * n + c0 + 64 * h + 4 * li) : vf4{0.f, 0.f, 0.f, 0.f};
-        float pv[KT];
+        for (int j = 0; j < PPT; ++j) {
+            const int e = threadIdx.x + 256 * j;
+            if (e < kStage * kp) ps[e / kp][e % kp] = pq[j];
+        }
+        __syncthreads();
+        if (sr + kStage < m) fetch(sr + kStage);  // next stage's loads overlap the MFMAs
 #pragma unroll
-        for (int t = 0; t < KT; ++t) pv[t] = pb[rr * kp + 16 * t + li];
+        for (int rg = 0; rg < 4; ++rg) {
+            const vf4 rv = *reinterpret_cast<const vf4*>(&slab[4 * rg + lg][64 * wave + 4 * li]);
+            float pv[KT];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int t = 0; t < KT; ++t) pv[t] = ps[4 * rg + lg][16 * t + li];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int t = 0; t < KT; ++t) acc[h][i][t] = mfma4(pv[t], rv[h][i], acc[h][i][t]);
-    }
-    // acc[h][i][t] lane: Q^T row 16 t + 4 lg + v, column c0 + 64 h + 4 li + i.
-    // Sum the four waves' partials in LDS, in wave order.
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int t = 0; t < KT; ++t)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            float& dst = red[16 * t + 4 * lg + v][64 * h + 4 * li + i];
-                            dst = (w == 0) ? acc[h][i][t][v] : dst + acc[h][i][t][v];
-                        }
+                for (int t = 0; t < KT; ++t) acc[i][t] = mfma4(pv[t], rv[i], acc[i][t]);
         }
         __syncthreads();
     }
+    // acc[i][t] lane: Q^T row 16 t + 4 lg + v, column c0 + 64 w + 4 li + i
     float* qtb = qt + b * kp * n;
-    for (int e = threadIdx.x; e < kp * kBackCols; e += 256) {
-        const int kk = e / kBackCols, cc = e % kBackCols;
-        if (c0 + cc < n) qtb[kk * n + c0 + cc] = red[kk][cc];
+    const int64_t wc = c0 + 64 * wave + 4 * li;
+    if (wc < n) {
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const vf4 o = vf4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
+                *reinterpret_cast<vf4*>(qtb + (16 * t + 4 * lg + v) * n + wc) = o;
+            }
     }
 }
 
 // ------------------------------------------------------------ quantize ----
-// blockIdx.x = 2 b + f: f = 0 quantizes U = P (m rows, row-major m x kp),
-// f = 1 quantizes V = Q (n rows, stored transposed as Q^T kp x n) and updates
-// q_state.  Per column: s = max|x| / 7, c = rint(x / s) in [-7, 7] (0 if s = 0).
+// Factor f of tensor b: f = 0 is U = P (m rows, row-major m x kp), f = 1 is V = Q
+// (n rows, stored transposed as Q^T kp x n).  Row blocks of 256 rows: blocks
+// [0, mb) cover U, [mb, mb + nb) cover V, for each tensor.
+// k_lr_colmax: per block and column, max |x| over the block's rows.
+// k_lr_pack:   s = (max over the factor's blocks) / 7; one row per thread:
+//              c = rint(x / s) clamped to [-7, 7] (0 if s = 0), nibbles packed low
+//              first along the rank index (or the fp32 factor copied); V's rows
+//              also refresh q_state where the column is alive.
+__device__ __forceinline__ float factor_elem(const float* x, int f, int64_t n, int kp, int64_t row, int kk) {
+    return f ? x[kk * n + row] : x[row * kp + kk];
+}
+
 template <int KT>
-__global__ __launch_bounds__(256) void k_lr_quantize(const float* __restrict__ p, const float* __restrict__ qt,
-                                                      const int* __restrict__ alive, int64_t m, int64_t n, int k,
-                                                      int factor_bits, float* __restrict__ q_state,
-                                                      void* __restrict__ u, float* __restrict__ u_scales,
-                                                      void* __restrict__ v, float* __restrict__ v_scales) {
+__global__ __launch_bounds__(256) void k_lr_colmax(const float* __restrict__ p, const float* __restrict__ qt,
+                                                    float* __restrict__ cmax, int64_t m, int64_t n) {
     constexpr int kp = 16 * KT;
-    constexpr int RPT = 256 / kp;  // threads per column in the max reduction
-    __shared__ float part[256];
-    __shared__ float sc[kp];
-    const int64_t b = blockIdx.x >> 1;
-    const int f = blockIdx.x & 1;
+    __shared__ float wmax[4][kp];
+    const int64_t mb = (m + 255) / 256, nb = (n + 255) / 256;
+    const int64_t b = blockIdx.x / (mb + nb);
+    const int64_t blk = blockIdx.x % (mb + nb);
+    const int f = blk >= mb;
+    const int64_t row = (f ? blk - mb : blk) * 256 + threadIdx.x;
     const int64_t rows = f ? n : m;
     const float* x = f ? qt + b * kp * n : p + b * m * kp;
-    // element (row, kk) of the factor
-    auto at = [&](int64_t row, int kk) -> float { return f ? x[kk * n + row] : x[row * kp + kk]; };
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float v[kp];
+    if (row >= rows) {
+#pragma unroll
+        for (int kk = 0; kk < kp; ++kk) v[kk] = 0.0f;
+    } else if (f) {  // Q^T: element kk of this row is x[kk * n + row] (coalesced over threads)
+#pragma unroll
+        for (int kk = 0; kk < kp; ++kk) v[kk] = fabsf(x[kk * n + row]);
+    } else {  // P: the row is kp consecutive floats
+#pragma unroll
+        for (int i = 0; i < kp; i += 4) {
+            const vf4 t = ld4(x + row * kp + i);
+            v[i] = fabsf(t[0]); v[i + 1] = fabsf(t[1]); v[i + 2] = fabsf(t[2]); v[i + 3] = fabsf(t[3]);
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kp; ++kk) {
+        float mx = v[kk];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (lane == 0) wmax[wave][kk] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x < kp) {
+        const int kk = threadIdx.x;
+        cmax[blockIdx.x * kp + kk] = fmaxf(fmaxf(wmax[0][kk], wmax[1][kk]), fmaxf(wmax[2][kk], wmax[3][kk]));
+    }
+}
 
+template <int KT>
+__global__ __launch_bounds__(256) void k_lr_pack(const float* __restrict__ p, const float* __restrict__ qt,
+                                                  const float* __restrict__ cmax, const int* __restrict__ alive,
+                                                  int64_t m, int64_t n, int k, int factor_bits,
+                                                  float* __restrict__ q_state, void* __restrict__ u,
+                                                  float* __restrict__ u_scales, void* __restrict__ v,
+                                                  float* __restrict__ v_scales) {
+    constexpr int kp = 16 * KT;
+    constexpr int TPC = 256 / kp;  // threads per column when reducing the block maxima
+    __shared__ float sc[kp];
+    __shared__ float part[kp][TPC];
+    const int64_t mb = (m + 255) / 256, nb = (n + 255) / 256;
+    const int64_t b = blockIdx.x / (mb + nb);
+    const int64_t blk = blockIdx.x % (mb + nb);
+    const int f = blk >= mb;
+    const int64_t fblk = f ? blk - mb : blk;
+    const int64_t row = fblk * 256 + threadIdx.x;
+    const int64_t rows = f ? n : m;
+    const float* x = f ? qt + b * kp * n : p + b * m * kp;
     if (factor_bits == 4) {
-        const int kk = tid % kp;
-        float mx = 0.0f;
-        for (int64_t row = tid / kp; row < rows; row += RPT) mx = fmaxf(mx, fabsf(at(row, kk)));
-        part[tid] = mx;
-        __syncthreads();
-        if (tid < kp) {
-            float mm = part[tid];
-            for (int q = 1; q < RPT; ++q) mm = fmaxf(mm, part[q * kp + tid]);
-            const float s = mm / 7.0f;
-            sc[tid] = s;
-            if (tid < k) (f ? v_scales : u_scales)[b * k + tid] = s;
+        if (threadIdx.x < kp * TPC) {
+            const int kk = threadIdx.x % kp, slot = threadIdx.x / kp;
+            const float* cm = cmax + (b * (mb + nb) + (f ? mb : 0)) * kp + kk;
+            float mm = 0.0f;
+            for (int64_t q = slot; q < (f ? nb : mb); q += TPC) mm = fmaxf(mm, cm[q * kp]);
+            part[kk][slot] = mm;
         }
         __syncthreads();
-        uint8_t* out = static_cast<uint8_t*>(f ? v : u) + b * rows * k / 2;
-        const int64_t nbytes = rows * k / 2;
-        for (int64_t e = tid; e < nbytes; e += 256) {
-            const int64_t row = (2 * e) / k;
-            const int kk0 = static_cast<int>((2 * e) % k);
-            uint32_t byte = 0;
+        if (threadIdx.x < kp) {
+            const int kk = threadIdx.x;
+            float mm = part[kk][0];
+            for (int q = 1; q < TPC; ++q) mm = fmaxf(mm, part[kk][q]);
+            const float s = mm / 7.0f;
+            sc[kk] = s;
+            if (fblk == 0 && kk < k) (f ? v_scales : u_scales)[b * k + kk] = s;
+        }
+        __syncthreads();
+        if (row < rows) {
+            float xv[kp];
+            if (f) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float s = sc[kk0 + h];
+                for (int kk = 0; kk < kp; ++kk) xv[kk] = x[kk * n + row];
+            } else {
+#pragma unroll
+                for (int i = 0; i < kp; i += 4) {
+                    const vf4 t = ld4(x + row * kp + i);
+                    xv[i] = t[0]; xv[i + 1] = t[1]; xv[i + 2] = t[2]; xv[i + 3] = t[3];
+                }
+            }
+            uint32_t words[kp / 8];
+#pragma unroll
+            for (int w = 0; w < kp / 8; ++w) words[w] = 0;
+#pragma unroll
+            for (int kk = 0; kk < kp; ++kk) {
+                const float s = sc[kk];
                 int c = 0;
-                if (s > 0.0f) {
-                    float q = rintf(at(row, kk0 + h) / s);
+                if (kk < k && s > 0.0f) {
+                    float q = rintf(xv[kk] / s);
                     q = fminf(fmaxf(q, -7.0f), 7.0f);
                     c = static_cast<int>(q);
                 }
-                byte |= (static_cast<uint32_t>(c) & 0xFu) << (4 * h);
+                words[kk / 8] |= (static_cast<uint32_t>(c) & 0xFu) << (4 * (kk % 8));
             }
-            out[e] = static_cast<uint8_t>(byte);
+            // the row's k/2 bytes start at a 16-byte boundary when k % 32 == 0 (one
+            // 16-byte store per 32 codes), at a 4-byte boundary when k % 8 == 0
+            uint8_t* out = static_cast<uint8_t*>(f ? v : u) + (b * rows + row) * k / 2;
+            if ((k & 31) == 0 && (reinterpret_cast<uintptr_t>(u) & 15) == 0 &&
+                (reinterpret_cast<uintptr_t>(v) & 15) == 0) {
+#pragma unroll
+                for (int w = 0; w < kp / 8; w += 4)
+                    if (8 * w < k)
+                        *reinterpret_cast<uint4*>(out + 4 * w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+            } else if ((k & 7) == 0) {
+#pragma unroll
+                for (int w = 0; w < kp / 8; ++w)
+                    if (8 * w < k) reinterpret_cast<uint32_t*>(out)[w] = words[w];
+            } else {
+                for (int q = 0; q < k / 2; ++q) out[q] = static_cast<uint8_t>(words[q / 4] >> (8 * (q % 4)));
+            }
         }
-    } else {
-        float* out = static_cast<float*>(f ? v : u) + b * rows * k;
-        for (int64_t e = tid; e < rows * k; e += 256) out[e] = at(e / k, static_cast<int>(e % k));
+    } else if (row < rows) {
+        float* out = static_cast<float*>(f ? v : u) + (b * rows + row) * k;
+        if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(f ? v : u) & 15) == 0) {
+#pragma unroll
+            for (int kk = 0; kk < kp; kk += 4) {
+                if (kk >= k) break;
+                *reinterpret_cast<vf4*>(out + kk) =
+                    vf4{factor_elem(x, f, n, kp, row, kk), factor_elem(x, f, n, kp, row, kk + 1),
+                        factor_elem(x, f, n, kp, row, kk + 2), factor_elem(x, f, n, kp, row, kk + 3)};
+            }
+        } else {
+            for (int kk = 0; kk < k; ++kk) out[kk] = factor_elem(x, f, n, kp, row, kk);
+        }
     }
-    if (f) {
-        float* qs = q_state + b * n * k;
+    if (f && row < rows) {
+        // q_state row = Q row where the column is alive, else its previous value;
+        // whole-row 16-byte stores when the layout allows (k % 4 == 0, aligned base)
+        float* qs = q_state + (b * n + row) * k;
         const int* al = alive + b * kp;
-        for (int64_t e = tid; e < n * k; e += 256) {
-            const int kk = static_cast<int>(e % k);
-            if (al[kk]) qs[e] = at(e / k, kk);
+        if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(q_state) & 15) == 0) {
+#pragma unroll
+            for (int kk = 0; kk < kp; kk += 4) {
+                if (kk >= k) break;
+                vf4 o = vf4{x[kk * n + row], x[(kk + 1) * n + row], x[(kk + 2) * n + row], x[(kk + 3) * n + row]};
+                if (!(al[kk] && al[kk + 1] && al[kk + 2] && al[kk + 3])) {
+                    const vf4 old = ld4(qs + kk);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (!al[kk + j]) o[j] = old[j];
+                }
+                *reinterpret_cast<vf4*>(qs + kk) = o;
+            }
+        } else {
+            for (int kk = 0; kk < k; ++kk)
+                if (al[kk]) qs[kk] = x[kk * n + row];
         }
     }
 }
 
 // --------------------------------------------------------- reconstruct ----
-// Workgroup: 4 waves side by side, each a 64 x 64 tile (4 x 4 MFMA tiles).
-// C'[i][j] = sum_kk V^[col i][kk] U^[row j][kk] = R^[row j][col i], so lane l holds
-// R^[row0 + 16 jt + li][col0 + 16 it + 4 lg .. + 3] after the k loop.
+// Workgroup: 4 waves over columns [c0, c0 + 256) and rows [r0, r0 + 64), in 4
+// stages of 16 rows.  Wave w owns columns c0 + 64 w .. + 63 (4 MFMA tiles) and keeps
+// their V^ operands in registers.  Per stage the MFMAs give
+// C'[i][j] = sum_kk V^[col i][kk] U^[row j][kk] = R^[row j][col i]  (lane l holds
+// R^[row0 + li][col + 4 lg .. + 3]); the 16 x 256 tile goes to LDS, then every wave
+// streams 4 whole rows: one load/store instruction covers 256 consecutive columns.
 template <int FB>
 __device__ __forceinline__ float factor_at(const void* f, const float* scales, int64_t row, int k, int kk) {
     if (kk >= k) return 0.0f;
@@ -428,23 +645,26 @@ __device__ __forceinline__ float factor_at(const void* f, const float* scales, i
     }
 }
 
-template <bool HAS_E, typename ActT, int FB>
+template <bool HAS_E, typename ActT, int FB, int KS>
 __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__ a, float* __restrict__ ahat,
                                                          float* __restrict__ err, const void* __restrict__ u,
                                                          const float* __restrict__ u_scales,
                                                          const void* __restrict__ v,
                                                          const float* __restrict__ v_scales, int64_t m,
                                                          int64_t n, int k, int64_t batch, int64_t total) {
+    constexpr int kStage = 16;
+    constexpr int kNS = kRecRows / kStage;
+    __shared__ float tile[kStage][kRecCols + 4];
+    __shared__ float uh[kRecRows][4 * KS + 1];  // dequantized U^ rows of this workgroup
     const int64_t rblocks = (m + kRecRows - 1) / kRecRows;
     const int64_t cblocks = (n + kRecCols - 1) / kRecCols;
     const int64_t lw = xcd_remap(blockIdx.x, total);
-    if (lw >= batch * rblocks * cblocks) return;
+    if (lw >= batch * rblocks * cblocks) return;  // uniform per workgroup
     const int64_t b = lw / (rblocks * cblocks);
-    const int64_t row0 = ((lw / cblocks) % rblocks) * kRecRows;
+    const int64_t r0 = ((lw / cblocks) % rblocks) * kRecRows;
+    const int64_t c0 = (lw % cblocks) * kRecCols;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int64_t col0 = (lw % cblocks) * kRecCols + 64 * wave;
-    if (col0 >= n) return;  // uniform per wave
 
     const int64_t usz = FB == 4 ? m * k / 2 : m * k * 4;  // bytes per tensor
     const int64_t vsz = FB == 4 ? n * k / 2 : n * k * 4;
@@ -452,44 +672,68 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     const void* vb = static_cast<const uint8_t*>(v) + b * vsz;
     const float* usb = FB == 4 ? u_scales + b * k : nullptr;
     const float* vsb = FB == 4 ? v_scales + b * k : nullptr;
+    const int64_t nrows = r0 + kRecRows < m ? kRecRows : m - r0;  // multiple of 16
+    const int nst = static_cast<int>(nrows / kStage);
 
-    bool jt_ok[4], it_ok[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        jt_ok[q] = row0 + 16 * q < m;
-        it_ok[q] = col0 + 16 * q < n;
+    for (int e = threadIdx.x; e < kRecRows * 4 * KS; e += 256) {
+        const int rr = e / (4 * KS), kk = e % (4 * KS);
+        uh[rr][kk] = rr < nrows ? factor_at<FB>(ub, usb, r0 + rr, k, kk) : 0.0f;
     }
-    vf4 acc[4][4];
+    // V^ operands of this wave's 4 column tiles, k-slice s: V^[col][4 s + lg].
+    const int64_t wc0 = c0 + 64 * wave;
+    float av[4][KS];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < 4; ++it) {
+        const int64_t col = wc0 + 16 * it + li;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) acc[it][jt] = vf4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = 0; 4 * s < k; ++s) {
-        const int kk = 4 * s + lg;
-        float bu[4], av[4];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) bu[jt] = jt_ok[jt] ? factor_at<FB>(ub, usb, row0 + 16 * jt + li, k, kk) : 0.0f;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) av[it] = it_ok[it] ? factor_at<FB>(vb, vsb, col0 + 16 * it + li, k, kk) : 0.0f;
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) acc[it][jt] = mfma4(av[it], bu[jt], acc[it][jt]);
+        for (int s = 0; s < KS; ++s) av[it][s] = col < n ? factor_at<FB>(vb, vsb, col, k, 4 * s + lg) : 0.0f;
     }
 
     const int64_t mn = m * n;
+    const int64_t col = c0 + 4 * lane;  // streaming column of this lane
+    const bool cok = col < n;
+    using RA = RawAct<ActT>;
+    vf4 hq[4];
+    typename RA::T xq[4];
+    auto load_stage = [&](int st) {
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        if (!jt_ok[jt]) continue;
+        for (int q = 0; q < 4; ++q) {
+            const int64_t off = b * mn + (r0 + kStage * st + 4 * wave + q) * n + col;
+            hq[q] = cok ? ld4_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (HAS_E) xq[q] = cok ? RA::load(a, off) : RA::zero();
+        }
+    };
+    load_stage(0);
+    __syncthreads();  // uh is complete
+    for (int st = 0; st < nst; ++st) {
+        vf4 acc[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            if (!it_ok[it]) continue;
-            const int64_t off = b * mn + (row0 + 16 * jt + li) * n + col0 + 16 * it + 4 * lg;
-            const vf4 hn = ld4_nt(ahat + off) + acc[it][jt];
-            st4_nt(ahat + off, hn);
-            if constexpr (HAS_E) st4_nt(err + off, act4(a, off) - hn);
+            acc[it] = vf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc[it] = mfma4(av[it][s], uh[kStage * st + li][4 * s + lg], acc[it]);
+            *reinterpret_cast<vf4*>(&tile[li][64 * wave + 16 * it + 4 * lg]) = acc[it];
         }
+        __syncthreads();
+        vf4 hc[4];
+        typename RA::T xc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hc[q] = hq[q];
+            if constexpr (HAS_E) xc[q] = xq[q];
+        }
+        if (st + 1 < nst) load_stage(st + 1);  // next stage's loads overlap this stage's stores
+        if (cok) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rr = 4 * wave + q;
+                const int64_t off = b * mn + (r0 + kStage * st + rr) * n + col;
+                const vf4 hn = hc[q] + *reinterpret_cast<const vf4*>(&tile[rr][4 * lane]);
+                st4_nt(ahat + off, hn);
+                if constexpr (HAS_E) st4_nt(err + off, RA::cvt(xc[q]) - hn);
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -500,6 +744,23 @@ template <typename K>
 hipError_t go(K kernel, int64_t blocks, void** args, hipStream_t stream) {
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)), dim3(256),
                            args, 0, stream);
+}
+
+// k-slices of the reconstruction: ceil(k / 4), instantiated for the rank buckets.
+template <bool HAS_E, typename ActT, int FB>
+hipError_t launch_reconstruct_fb(int k, int64_t total, void** args, hipStream_t stream) {
+    const int ks = (k + 3) / 4;
+    if (ks <= 2) return go(&k_lr_reconstruct<HAS_E, ActT, FB, 2>, total, args, stream);
+    if (ks <= 4) return go(&k_lr_reconstruct<HAS_E, ActT, FB, 4>, total, args, stream);
+    if (ks <= 8) return go(&k_lr_reconstruct<HAS_E, ActT, FB, 8>, total, args, stream);
+    if (ks <= 12) return go(&k_lr_reconstruct<HAS_E, ActT, FB, 12>, total, args, stream);
+    return go(&k_lr_reconstruct<HAS_E, ActT, FB, 16>, total, args, stream);
+}
+
+template <bool HAS_E, typename ActT>
+hipError_t launch_reconstruct(int factor_bits, int k, int64_t total, void** args, hipStream_t stream) {
+    return factor_bits == 4 ? launch_reconstruct_fb<HAS_E, ActT, 4>(k, total, args, stream)
+                            : launch_reconstruct_fb<HAS_E, ActT, 32>(k, total, args, stream);
 }
 
 template <typename ActT, int KT>
@@ -522,15 +783,23 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         e = it == 0 ? go(&k_lr_project<true, ActT, KT>, ptotal, pargs, stream)
                     : go(&k_lr_project<false, ActT, KT>, ptotal, pargs, stream);
         if (e != hipSuccess) return e;
-        void* oargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.alive, &m, &nseg, &k};
-        if ((e = go(&k_lr_orth<KT>, batch, oargs, stream)) != hipSuccess) return e;
+        int64_t gblocks = (m + GramShape<KT>::rows - 1) / GramShape<KT>::rows;
+        void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch};
+        if ((e = go(&k_lr_gram<KT>, batch * gblocks, gargs, stream)) != hipSuccess) return e;
+        void* cargs[] = {(void*)&ws.gpart, (void*)&ws.xinv, (void*)&ws.alive, &gblocks, &k};
+        if ((e = go(&k_lr_chol<KT>, batch, cargs, stream)) != hipSuccess) return e;
+        void* sargs[] = {(void*)&ws.p, (void*)&ws.xinv, &m, &batch};
+        if ((e = go(&k_lr_solve<KT>, batch * ((m + 255) / 256), sargs, stream)) != hipSuccess) return e;
         void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal};
         if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
     }
     {
-        void* qargs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.alive, &m, &n, &k, &factor_bits,
-                         &q_state, &u, &u_scales, &v, &v_scales};
-        if ((e = go(&k_lr_quantize<KT>, 2 * batch, qargs, stream)) != hipSuccess) return e;
+        const int64_t qblocks = batch * ((m + 255) / 256 + (n + 255) / 256);
+        void* margs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.cmax, &m, &n};
+        if ((e = go(&k_lr_colmax<KT>, qblocks, margs, stream)) != hipSuccess) return e;
+        void* qargs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.cmax, (void*)&ws.alive, &m, &n, &k,
+                         &factor_bits, &q_state, &u, &u_scales, &v, &v_scales};
+        if ((e = go(&k_lr_pack<KT>, qblocks, qargs, stream)) != hipSuccess) return e;
     }
     int64_t rtotal = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
     const void* uc = u;
@@ -538,8 +807,7 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     const float* usc = u_scales;
     const float* vsc = v_scales;
     void* rargs[] = {&a, &ahat, &err, &uc, &usc, &vc, &vsc, &m, &n, &k, &batch, &rtotal};
-    return factor_bits == 4 ? go(&k_lr_reconstruct<true, ActT, 4>, rtotal, rargs, stream)
-                            : go(&k_lr_reconstruct<true, ActT, 32>, rtotal, rargs, stream);
+    return launch_reconstruct<true, ActT>(factor_bits, k, rtotal, rargs, stream);
 }
 
 template <typename ActT>
@@ -559,21 +827,36 @@ hipError_t dispatch_rank(const ActT* a, float* ahat, float* err, int64_t m, int6
 LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch, size_t* bytes) {
     const int64_t kp = (rank + 15) / 16 * 16;
     const int64_t nseg = (n + kSegCols - 1) / kSegCols;
+    const int64_t grows = kp == 16 ? 256 : (kp == 32 ? 128 : 64);  // GramShape<kp / 16>::rows
+    const int64_t gblocks = (m + grows - 1) / grows;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t sz_r = up(batch * m * n * 4);
     const int64_t sz_qt = up(batch * kp * n * 4);
     const int64_t sz_y = up(batch * nseg * m * kp * 4);
     const int64_t sz_p = up(batch * m * kp * 4);
     const int64_t sz_al = up(batch * kp * 4);
-    if (bytes) *bytes = static_cast<size_t>(sz_r + sz_qt + sz_y + sz_p + sz_al);
+    const int64_t sz_g = up(batch * gblocks * kp * kp * 8);
+    const int64_t sz_x = up(batch * kp * kp * 8);
+    const int64_t sz_c = up(batch * ((m + 255) / 256 + (n + 255) / 256) * kp * 4);
+    if (bytes) *bytes = static_cast<size_t>(sz_r + sz_qt + sz_y + sz_p + sz_al + sz_g + sz_x + sz_c);
     LowrankWorkspace ws{};
     if (base) {
         char* c = static_cast<char*>(base);
         ws.r = reinterpret_cast<float*>(c);
-        ws.qt = reinterpret_cast<float*>(c + sz_r);
-        ws.ypart = reinterpret_cast<float*>(c + sz_r + sz_qt);
-        ws.p = reinterpret_cast<float*>(c + sz_r + sz_qt + sz_y);
-        ws.alive = reinterpret_cast<int*>(c + sz_r + sz_qt + sz_y + sz_p);
+        c += sz_r;
+        ws.qt = reinterpret_cast<float*>(c);
+        c += sz_qt;
+        ws.ypart = reinterpret_cast<float*>(c);
+        c += sz_y;
+        ws.p = reinterpret_cast<float*>(c);
+        c += sz_p;
+        ws.alive = reinterpret_cast<int*>(c);
+        c += sz_al;
+        ws.gpart = reinterpret_cast<double*>(c);
+        c += sz_g;
+        ws.xinv = reinterpret_cast<double*>(c);
+        c += sz_x;
+        ws.cmax = reinterpret_cast<float*>(c);
     }
     return ws;
 }
@@ -598,8 +881,7 @@ hipError_t launch_lowrank_decompress(int factor_bits, const void* u, const float
     float* err = nullptr;
     int k = rank;
     void* args[] = {&a, &ahat, &err, &u, &u_scales, &v, &v_scales, &m, &n, &k, &batch, &rtotal};
-    return factor_bits == 4 ? go(&k_lr_reconstruct<false, uint16_t, 4>, rtotal, args, stream)
-                            : go(&k_lr_reconstruct<false, uint16_t, 32>, rtotal, args, stream);
+    return launch_reconstruct<false, uint16_t>(factor_bits, k, rtotal, args, stream);
 }
 
 }  // namespace cf

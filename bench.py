@@ -39,6 +39,20 @@ BYTES_PER_ELEM = {
     "decode2": 4 + 4 + 2 / 8 + 4 / 128,
     "init": 2 + 4 + 4,
 }
+
+
+def lowrank_bytes_per_elem(iters: int) -> float:
+    """Algorithmic HBM bytes per element of one low-rank step: the first projection
+    reads a and Ahat and writes r (10 B), each further projection and each
+    back-projection reads r (4 B), the reconstruction reads a and Ahat and writes
+    Ahat and e (14 B)."""
+    return 10 + 4 * (iters - 1) + 4 * iters + 14
+
+
+def lowrank_flops_per_elem(rank: int, iters: int) -> float:
+    """Algorithmic flops per element: 2k per projection and per back-projection pass,
+    2k for the reconstruction."""
+    return 4 * rank * iters + 2 * rank
 KERNEL_SRC = os.path.join(ROOT, "activation_residual_compression_cf_amd", "csrc", "cf_quant.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "compress_q1_flux_pmc.md")
 
@@ -323,6 +337,39 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
     row("compress1_flux_per_layer", ms, "compress1")
     del s1
     torch.cuda.empty_cache()
+    # Compact-Lowrank on the FLUX shard: one call per step over all 114 tensors
+    for rank, iters in ((32, 2), (8, 10)):
+        ahat = torch.empty((wl.slots, wl.m, wl.n), dtype=torch.float32, device=dev)
+        err = torch.empty_like(ahat)
+        cf.init_state(steps_d[0], ahat, err)
+        qs = torch.from_numpy(np.stack([gen.start_basis(0, s, wl.n, rank)
+                                        for s in range(wl.slots)])).to(dev)
+        ws = torch.empty(cf.lowrank_workspace_bytes(wl.m, wl.n, rank, wl.slots), dtype=torch.uint8,
+                         device=dev)
+        pay = cf.lowrank_payload(wl.slots, wl.m, wl.n, rank, 4, dev)
+        a3 = [steps_d[c].view(wl.slots, wl.m, wl.n) for c in compressed]
+        cf.lowrank_compress(a3[0], ahat, err, qs, rank, iters, 4, pay, ws)
+        it4 = iter(range(10 ** 9))
+        ms = time_calls(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat,
+                                                           err, qs, rank, iters, 4, pay, ws), 4)
+        bpe = lowrank_bytes_per_elem(iters)
+        fpe = lowrank_flops_per_elem(rank, iters)
+        hbm = step_elems * bpe / (ms / 1e3) / 1e9
+        name = f"lowrank_r{rank}_q{iters}_int4_flux"
+        rows[name] = {"ms_per_step": round(ms, 4), "act_GBs": round(step_elems * 2 / (ms / 1e3) / 1e9, 1),
+                      "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
+                      "tflops": round(step_elems * fpe / (ms / 1e3) / 1e12, 2),
+                      "bytes_per_elem": bpe, "flops_per_elem": fpe,
+                      "payload_bytes_per_tensor": wl.m * rank // 2 + wl.n * rank // 2 + 8 * rank}
+        log(f"{name}: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM, "
+            f"{rows[name]['tflops']} TFLOP/s")
+        rx = torch.empty_like(ahat)
+        cf.init_state(steps_d[0], rx)
+        ms = time_calls(torch, lambda: cf.lowrank_decompress(4, pay, rx, rank), 4)
+        rows[f"lowrank_r{rank}_decode_flux"] = {"ms_per_step": round(ms, 4),
+                                               "hbm_frac": round(step_elems * 8 / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del ahat, err, qs, ws, pay, rx
+        torch.cuda.empty_cache()
     # CogVideoX-shaped shard, Compact-2bit
     cw = gen.WORKLOADS["cogvideo"]
     tr = gen.Trajectory(cw, 0)
