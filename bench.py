@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
+    ap.add_argument("--rows", default="",
+                    help="comma-separated name prefixes of the secondary rows to run (default all)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -242,7 +244,8 @@ def main():
 
     rows = {}
     if not args.no_rows:
-        rows = secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call)
+        want = [w for w in args.rows.split(",") if w]
+        rows = secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -290,11 +293,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
-    """The other rows of the path, each timed with events over whole steps."""
+def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want=()):
+    """The other rows of the path, each timed with events over whole steps.  `want`
+    selects rows by name prefix (all when empty)."""
     numel = wl.numel
     rows = {}
     step_elems = wl.slots * numel
+
+    def on(name):
+        return not want or any(name.startswith(w) for w in want)
 
     def row(name, ms, bytes_key, elems=step_elems):
         gbs_act = elems * 2 / (ms / 1e3) / 1e9
@@ -303,7 +310,21 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
                       "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4)}
         log(f"{name}: {ms:.3f} ms/step, {gbs_act:.0f} GB/s act, {hbm / HBM_PEAK_GBS:.1%} of HBM")
 
-    # 2-bit compress on the same shard
+    # 2-bit compress on the same shard, its receiver decode, 1-bit decode and init
+    if on("compress2_flux") or on("decode") or on("init"):
+        quant_rows(torch, cf, dev, wl, steps_d, compressed, per_call, row, on)
+    if on("compress1_flux_per_layer"):
+        per_layer_row(torch, cf, dev, wl, steps_d, compressed, row)
+    if on("lowrank"):
+        lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on)
+    if on("compress2_cogvideo"):
+        cogvideo_row(torch, np, cf, gen, dev, per_call, row)
+    torch.cuda.empty_cache()
+    return rows
+
+
+def quant_rows(torch, cf, dev, wl, steps_d, compressed, per_call, row, on):
+    numel = wl.numel
     s2 = cf.Slab(wl.slots, numel, 2, dev)
     s2.init(steps_d[0], per_call)
     s2.compress(steps_d[compressed[0]], per_call)
@@ -328,7 +349,11 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
     ms = time_calls(torch, lambda: s1.init(steps_d[0], per_call), 8)
     row("init_flux", ms, "init")
     del s1, s2, rx
-    # per-layer pattern: 57 back-to-back calls of one layer's K and V
+
+
+def per_layer_row(torch, cf, dev, wl, steps_d, compressed, row):
+    """Per-layer pattern: 57 back-to-back calls of one layer's K and V."""
+    numel = wl.numel
     s1 = cf.Slab(wl.slots, numel, 1, dev)
     s1.init(steps_d[0], 2)
     it2 = iter(range(10 ** 9))
@@ -337,8 +362,13 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
     row("compress1_flux_per_layer", ms, "compress1")
     del s1
     torch.cuda.empty_cache()
-    # Compact-Lowrank on the FLUX shard: one call per step over all 114 tensors
+
+
+def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on):
+    """Compact-Lowrank on the FLUX shard: one call per step over all 114 tensors."""
     for rank, iters in ((32, 2), (8, 10)):
+        if not on(f"lowrank_r{rank}_q{iters}"):
+            continue
         ahat = torch.empty((wl.slots, wl.m, wl.n), dtype=torch.float32, device=dev)
         err = torch.empty_like(ahat)
         cf.init_state(steps_d[0], ahat, err)
@@ -370,7 +400,10 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
                                                "hbm_frac": round(step_elems * 8 / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         del ahat, err, qs, ws, pay, rx
         torch.cuda.empty_cache()
-    # CogVideoX-shaped shard, Compact-2bit
+
+
+def cogvideo_row(torch, np, cf, gen, dev, per_call, row):
+    """CogVideoX-shaped shard, Compact-2bit."""
     cw = gen.WORKLOADS["cogvideo"]
     tr = gen.Trajectory(cw, 0)
     cs = [torch.from_numpy(tr.next().view(np.int16)).to(dev).view(torch.bfloat16) for _ in range(4)]
@@ -381,8 +414,6 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call):
     ms = time_calls(torch, lambda: sc.compress(cs[2 + next(it3) % 2], per_call), 8)
     row("compress2_cogvideo", ms, "compress2", cw.slots * cw.numel)
     del sc, cs
-    torch.cuda.empty_cache()
-    return rows
 
 
 if __name__ == "__main__":
