@@ -17,6 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcf.so")
 
 CF_BF16, CF_F32 = 0, 1
+CF_MODE_NOEF, CF_MODE_NAIVE = 1, 2
 GROUP = 128
 
 STATUS = {0: "CF_OK", -1: "CF_E_NULL", -2: "CF_E_SHAPE", -3: "CF_E_ALIGN", -4: "CF_E_ARG",
@@ -27,6 +28,8 @@ _SIG = {
     "cf_init_state": ("i", "ippplp"),
     "cf_compress": ("i", "iippppplp"),
     "cf_decompress": ("i", "ippplp"),
+    "cf_decompress_bf16": ("i", "ipppplp"),
+    "cf_compress_ablation": ("i", "iiipppppl" "p"),
     "cf_lowrank_compress": ("i", "ipppllii" "iipppppp" "zp"),
     "cf_lowrank_decompress": ("i", "ipppp" "pllii" "p"),
     "cf_lowrank_workspace_bytes": ("z", "llii"),
@@ -142,10 +145,32 @@ def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
 
 
 def decompress(bits: int, codes: torch.Tensor, scales: torch.Tensor, ahat: torch.Tensor,
-               stream=None):
-    """Receiver step: ahat += decoded residual."""
-    _check("cf_decompress", lib.cf_decompress(bits, _ptr(codes), _ptr(scales), _ptr(ahat),
-                                              ahat.numel(), _stream(stream)))
+               stream=None, out_bf16: torch.Tensor | None = None):
+    """Receiver step: ahat += decoded residual; with out_bf16 (a bfloat16 tensor of the
+    same size) also writes the updated reconstruction rounded to bf16."""
+    if out_bf16 is None:
+        _check("cf_decompress", lib.cf_decompress(bits, _ptr(codes), _ptr(scales), _ptr(ahat),
+                                                  ahat.numel(), _stream(stream)))
+        return
+    if out_bf16.dtype != torch.bfloat16 or out_bf16.numel() != ahat.numel():
+        raise ValueError("out_bf16 must be a bfloat16 tensor of ahat's size")
+    _check("cf_decompress_bf16", lib.cf_decompress_bf16(bits, _ptr(codes), _ptr(scales), _ptr(ahat),
+                                                        _ptr(out_bf16), ahat.numel(), _stream(stream)))
+
+
+def compress_ablation(mode: int, bits: int, a: torch.Tensor, ahat: torch.Tensor,
+                      a_prev: torch.Tensor | None = None, codes: torch.Tensor | None = None,
+                      scales: torch.Tensor | None = None, stream=None):
+    """Ablation sender step (CF_MODE_NOEF needs a_prev); returns (codes, scales)."""
+    n = a.numel()
+    if codes is None:
+        codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty(n // GROUP, dtype=torch.float32, device=a.device)
+    _check("cf_compress_ablation", lib.cf_compress_ablation(
+        mode, bits, _act_dtype(a), _ptr(a), _ptr(a_prev), _ptr(ahat), _ptr(codes), _ptr(scales), n,
+        _stream(stream)))
+    return codes, scales
 
 
 def _dev_ptr(t: torch.Tensor) -> int:

@@ -138,8 +138,48 @@ int cf_decompress(int bits, const uint8_t* codes, const float* scales, float* ah
     const bool out[3] = {false, false, true};
     if (any_alias(r, out)) return CF_E_ALIAS;
     if (int rc = check_device()) return rc;
-    return cf::launch_decompress(bits, codes, scales, ahat, numel, static_cast<hipStream_t>(stream)) ==
+    return cf::launch_decompress(bits, codes, scales, ahat, nullptr, numel, static_cast<hipStream_t>(stream)) ==
                    hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
+int cf_decompress_bf16(int bits, const uint8_t* codes, const float* scales, float* ahat, uint16_t* out,
+                       int64_t numel, void* stream) {
+    if (bits != 1 && bits != 2) return CF_E_ARG;
+    if (!codes || !scales || !ahat || !out) return CF_E_NULL;
+    if (int rc = valid_numel(numel)) return rc;
+    if (!aligned16(codes) || !aligned4(scales) || !aligned16(ahat) || !aligned16(out)) return CF_E_ALIGN;
+    const Range r[4] = {range_of(codes, numel * bits / 8), range_of(scales, numel / CF_GROUP * 4),
+                        range_of(ahat, numel * 4), range_of(out, numel * 2)};
+    const bool is_out[4] = {false, false, true, true};
+    if (any_alias(r, is_out)) return CF_E_ALIAS;
+    if (int rc = check_device()) return rc;
+    return cf::launch_decompress(bits, codes, scales, ahat, out, numel, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
+int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const void* a_prev, float* ahat,
+                         uint8_t* codes, float* scales, int64_t numel, void* stream) {
+    if ((mode != CF_MODE_NOEF && mode != CF_MODE_NAIVE) || (bits != 1 && bits != 2) ||
+        (a_dtype != CF_BF16 && a_dtype != CF_F32))
+        return CF_E_ARG;
+    if (!a || !ahat || !codes || !scales || (mode == CF_MODE_NOEF && !a_prev)) return CF_E_NULL;
+    if (int rc = valid_numel(numel)) return rc;
+    if (!aligned16(a) || (a_prev && !aligned16(a_prev)) || !aligned16(ahat) || !aligned16(codes) ||
+        !aligned4(scales))
+        return CF_E_ALIGN;
+    const Range r[5] = {range_of(a, act_bytes(a_dtype, numel)),
+                        range_of(a_prev, mode == CF_MODE_NOEF ? act_bytes(a_dtype, numel) : 0),
+                        range_of(ahat, numel * 4), range_of(codes, numel * bits / 8),
+                        range_of(scales, numel / CF_GROUP * 4)};
+    const bool is_out[5] = {false, false, true, true, true};
+    if (any_alias(r, is_out)) return CF_E_ALIAS;
+    if (int rc = check_device()) return rc;
+    return cf::launch_compress_ablation(mode, bits, a_dtype, a, a_prev, ahat, codes, scales, numel,
+                                        static_cast<hipStream_t>(stream)) == hipSuccess
                ? CF_OK
                : CF_E_HIP;
 }

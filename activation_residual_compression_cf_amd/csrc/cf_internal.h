@@ -14,7 +14,11 @@ hipError_t launch_init(int a_dtype, const void* a, float* ahat, float* err, int6
                        hipStream_t stream);
 hipError_t launch_compress(int bits, int a_dtype, const void* a, float* ahat, float* err,
                            uint8_t* codes, float* scales, int64_t numel, hipStream_t stream);
-hipError_t launch_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat,
+hipError_t launch_compress_ablation(int mode, int bits, int a_dtype, const void* a, const void* a_prev,
+                                    float* ahat, uint8_t* codes, float* scales, int64_t numel,
+                                    hipStream_t stream);
+// out (bf16 bits of the updated reconstruction) may be null.
+hipError_t launch_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat, uint16_t* out,
                              int64_t numel, hipStream_t stream);
 
 // Low-rank workspace regions (carved from one caller buffer).

@@ -74,10 +74,17 @@ __device__ __forceinline__ vf4 dequant4(uint32_t c, float s) {
                dequant<BITS>(c >> (3 * BITS), s)};
 }
 
-template <int BITS, typename ActT, int IPS, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
-                                                     float* __restrict__ err, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales, int64_t ngroups) {
+// Sender modes.  kEF: r = a - ahat; ahat += d; err = a - ahat (the method).
+// kNoEF (ablation without error feedback): r = a - a_prev; ahat += d (the receiver's
+// mirror); no err.  kNaive (ablation: the activation itself is quantized): r = a;
+// ahat = d; no err.
+enum SenderMode { kEF = 0, kNoEF = 1, kNaive = 2 };
+
+template <int BITS, typename ActT, int IPS, int BLOCK, int MODE>
+__global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, const ActT* __restrict__ a_prev,
+                                                     float* __restrict__ ahat, float* __restrict__ err,
+                                                     uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                     int64_t ngroups) {
     constexpr int kWaves = BLOCK / 64;
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;  // lane within the half wave that owns a group
@@ -95,7 +102,14 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
         gi[k] = ok[k] ? g : ngroups - 1;  // ragged tail: reload the last group, skip the stores
         const int64_t off = gi[k] * kGroup + hl * 4;
         x[k] = load_act4(a, off);
-        h[k] = ld_nt(ahat + off);
+        if constexpr (MODE == kNoEF) h[k] = load_act4(a_prev, off);  // reference: previous activation
+        else if constexpr (MODE == kEF) h[k] = ld_nt(ahat + off);
+        else h[k] = vf4{0.f, 0.f, 0.f, 0.f};
+    }
+    vf4 hprev[IPS];
+    if constexpr (MODE == kNoEF) {
+#pragma unroll
+        for (int k = 0; k < IPS; ++k) hprev[k] = ld_nt(ahat + gi[k] * kGroup + hl * 4);
     }
 
 #pragma unroll
@@ -132,8 +146,16 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
                 code |= (sign | (mag << 1)) << (2 * i);
             }
         }
-        const vf4 hn = h[k] + dequant4<BITS>(code, s);
-        const vf4 e = x[k] - hn;
+        const vf4 d = dequant4<BITS>(code, s);
+        vf4 hn, e;
+        if constexpr (MODE == kEF) {
+            hn = h[k] + d;
+            e = x[k] - hn;
+        } else if constexpr (MODE == kNoEF) {
+            hn = hprev[k] + d;
+        } else {
+            hn = d;
+        }
 
         // Gather the group's codes into dwords: 1-bit lanes hold a nibble (8 lanes
         // per dword), 2-bit lanes a byte (4 lanes per dword).
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
         if (ok[k]) {
             const int64_t off = gi[k] * kGroup + hl * 4;
             st_nt(ahat + off, hn);
-            st_nt(err + off, e);
+            if constexpr (MODE == kEF) st_nt(err + off, e);
             if constexpr (BITS == 1) {
                 if ((hl & 7) == 0) *reinterpret_cast<uint32_t*>(codes + gi[k] * 16 + (hl >> 1)) = w;
             } else {
@@ -161,10 +183,22 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
     }
 }
 
-template <int BITS, int IPS, int BLOCK>
+// Round-to-nearest-even bf16 of 4 finite floats, packed as 2 words.
+__device__ __forceinline__ vu2 to_bf16x4(vf4 v) {
+    uint32_t q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __float_as_uint(v[i]);
+        q[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    }
+    return vu2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
+}
+
+template <int BITS, int IPS, int BLOCK, bool OUT16>
 __global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict__ codes,
                                                        const float* __restrict__ scales,
-                                                       float* __restrict__ ahat, int64_t ngroups) {
+                                                       float* __restrict__ ahat, uint16_t* __restrict__ out,
+                                                       int64_t ngroups) {
     constexpr int kWaves = BLOCK / 64;
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;
@@ -193,7 +227,11 @@ __global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict_
 #pragma unroll
     for (int k = 0; k < IPS; ++k) {
         const vf4 hn = h[k] + dequant4<BITS>(code[k], s[k]);
-        if (ok[k]) st_nt(ahat + gi[k] * kGroup + hl * 4, hn);
+        if (ok[k]) {
+            const int64_t off = gi[k] * kGroup + hl * 4;
+            st_nt(ahat + off, hn);
+            if constexpr (OUT16) __builtin_nontemporal_store(to_bf16x4(hn), reinterpret_cast<vu2*>(out + off));
+        }
     }
 }
 
@@ -219,20 +257,30 @@ hipError_t launch(K kernel, int64_t ngroups, int ips, int block, void** args, hi
                            dim3(block), args, 0, stream);
 }
 
-template <int BITS, typename ActT>
-hipError_t run_compress(const ActT* a, float* ahat, float* err, uint8_t* codes, float* scales,
-                        int64_t ngroups, hipStream_t stream) {
-    void* args[] = {&a, &ahat, &err, &codes, &scales, &ngroups};
-    if (ngroups >= kLargeCall) return launch(&k_compress<BITS, ActT, 1, 256>, ngroups, 1, 256, args, stream);
-    return launch(&k_compress<BITS, ActT, 2, 128>, ngroups, 2, 128, args, stream);
+template <int BITS, typename ActT, int MODE>
+hipError_t run_compress(const ActT* a, const ActT* a_prev, float* ahat, float* err, uint8_t* codes,
+                        float* scales, int64_t ngroups, hipStream_t stream) {
+    void* args[] = {&a, &a_prev, &ahat, &err, &codes, &scales, &ngroups};
+    if (ngroups >= kLargeCall)
+        return launch(&k_compress<BITS, ActT, 1, 256, MODE>, ngroups, 1, 256, args, stream);
+    return launch(&k_compress<BITS, ActT, 2, 128, MODE>, ngroups, 2, 128, args, stream);
 }
 
-template <int BITS>
-hipError_t run_decompress(const uint8_t* codes, const float* scales, float* ahat, int64_t ngroups,
+template <typename ActT, int MODE>
+hipError_t compress_bits(int bits, const void* a, const void* a_prev, float* ahat, float* err, uint8_t* codes,
+                         float* scales, int64_t ng, hipStream_t stream) {
+    const auto* x = static_cast<const ActT*>(a);
+    const auto* xp = static_cast<const ActT*>(a_prev);
+    return bits == 1 ? run_compress<1, ActT, MODE>(x, xp, ahat, err, codes, scales, ng, stream)
+                     : run_compress<2, ActT, MODE>(x, xp, ahat, err, codes, scales, ng, stream);
+}
+
+template <int BITS, bool OUT16>
+hipError_t run_decompress(const uint8_t* codes, const float* scales, float* ahat, uint16_t* out, int64_t ngroups,
                           hipStream_t stream) {
-    void* args[] = {&codes, &scales, &ahat, &ngroups};
-    if (ngroups >= kLargeCall) return launch(&k_decompress<BITS, 1, 256>, ngroups, 1, 256, args, stream);
-    return launch(&k_decompress<BITS, 2, 128>, ngroups, 2, 128, args, stream);
+    void* args[] = {&codes, &scales, &ahat, &out, &ngroups};
+    if (ngroups >= kLargeCall) return launch(&k_decompress<BITS, 1, 256, OUT16>, ngroups, 1, 256, args, stream);
+    return launch(&k_decompress<BITS, 2, 128, OUT16>, ngroups, 2, 128, args, stream);
 }
 
 template <typename ActT>
@@ -255,21 +303,29 @@ hipError_t launch_init(int a_dtype, const void* a, float* ahat, float* err, int6
 hipError_t launch_compress(int bits, int a_dtype, const void* a, float* ahat, float* err,
                            uint8_t* codes, float* scales, int64_t numel, hipStream_t stream) {
     const int64_t ng = numel / kGroup;
-    if (a_dtype == 0) {
-        const auto* ab = static_cast<const uint16_t*>(a);
-        return bits == 1 ? run_compress<1>(ab, ahat, err, codes, scales, ng, stream)
-                         : run_compress<2>(ab, ahat, err, codes, scales, ng, stream);
-    }
-    const auto* af = static_cast<const float*>(a);
-    return bits == 1 ? run_compress<1>(af, ahat, err, codes, scales, ng, stream)
-                     : run_compress<2>(af, ahat, err, codes, scales, ng, stream);
+    return a_dtype == 0 ? compress_bits<uint16_t, kEF>(bits, a, nullptr, ahat, err, codes, scales, ng, stream)
+                        : compress_bits<float, kEF>(bits, a, nullptr, ahat, err, codes, scales, ng, stream);
 }
 
-hipError_t launch_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat,
+hipError_t launch_compress_ablation(int mode, int bits, int a_dtype, const void* a, const void* a_prev,
+                                    float* ahat, uint8_t* codes, float* scales, int64_t numel,
+                                    hipStream_t stream) {
+    const int64_t ng = numel / kGroup;
+    if (mode == kNoEF)
+        return a_dtype == 0 ? compress_bits<uint16_t, kNoEF>(bits, a, a_prev, ahat, nullptr, codes, scales, ng, stream)
+                            : compress_bits<float, kNoEF>(bits, a, a_prev, ahat, nullptr, codes, scales, ng, stream);
+    return a_dtype == 0 ? compress_bits<uint16_t, kNaive>(bits, a, nullptr, ahat, nullptr, codes, scales, ng, stream)
+                        : compress_bits<float, kNaive>(bits, a, nullptr, ahat, nullptr, codes, scales, ng, stream);
+}
+
+hipError_t launch_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat, uint16_t* out,
                              int64_t numel, hipStream_t stream) {
     const int64_t ng = numel / kGroup;
-    return bits == 1 ? run_decompress<1>(codes, scales, ahat, ng, stream)
-                     : run_decompress<2>(codes, scales, ahat, ng, stream);
+    if (out)
+        return bits == 1 ? run_decompress<1, true>(codes, scales, ahat, out, ng, stream)
+                         : run_decompress<2, true>(codes, scales, ahat, out, ng, stream);
+    return bits == 1 ? run_decompress<1, false>(codes, scales, ahat, nullptr, ng, stream)
+                     : run_decompress<2, false>(codes, scales, ahat, nullptr, ng, stream);
 }
 
 }  // namespace cf

@@ -60,6 +60,9 @@ enum {
 
 enum { CF_BF16 = 0, CF_F32 = 1 };
 
+/* Sender modes of cf_compress_ablation. */
+enum { CF_MODE_NOEF = 1, CF_MODE_NAIVE = 2 };
+
 #define CF_GROUP 128
 
 /*
@@ -101,6 +104,32 @@ int cf_compress(int bits, int a_dtype, const void* a, float* ahat, float* err, u
  */
 int cf_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat, int64_t numel,
                   void* stream);
+
+/*
+ * Receiver step with a bf16 copy for the consumer (the attention that reads the
+ * reconstructed K/V): exactly cf_decompress, and then out[i] = the
+ * round-to-nearest-even bf16 of the updated ahat[i].  Decoding several peers'
+ * payloads is one call when their codes, scales, mirrors and outputs are laid out
+ * back to back (peer p at offset p * numel_per_peer).
+ *   out: numel bf16 (raw 16-bit storage), 16-byte aligned, out.
+ */
+int cf_decompress_bf16(int bits, const uint8_t* codes, const float* scales, float* ahat, uint16_t* out,
+                       int64_t numel, void* stream);
+
+/*
+ * Ablation modes of the sender, for studies of the method's design (measured-
+ * effects table: "Add residual compression with error feedback"; Surprising
+ * findings: naive 1-bit compression of full activations collapses).  Same
+ * quantizer, codes and scales as cf_compress; per group:
+ *   CF_MODE_NOEF:  r = a - a_prev (the raw step delta, no error feedback);
+ *                  ahat = ahat + d (the receiver's mirror, which cf_decompress
+ *                  reproduces); a_prev: numel of a_dtype, in.
+ *   CF_MODE_NAIVE: r = a (the activation itself); ahat = d (its decoded value);
+ *                  a_prev unused (may be NULL).
+ * No error buffer is kept in either mode.
+ */
+int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const void* a_prev, float* ahat,
+                         uint8_t* codes, float* scales, int64_t numel, void* stream);
 
 /*
  * Sender step, Compact-Lowrank (Approach: low-rank compression of the residual

@@ -162,3 +162,25 @@ def test_lowrank_validation(L):
                                    P(0x500000), 64, 128, 8, 1, None) == CF_E_ALIAS
     assert L.cf_lowrank_decompress(4, P(0x500000), P(0x600000), P(0x700000), P(0x800000),
                                    P(0x200000), 64, 128, 8, 1, None) == CF_E_DEVICE
+
+
+def test_ablation_and_bf16_decode_validation(L):
+    L.cf_compress_ablation.argtypes = ([ctypes.c_int] * 3 + [ctypes.c_void_p] * 5 +
+                                       [ctypes.c_int64, ctypes.c_void_p])
+    call = lambda mode, ap=0x200000, n=1280, bits=1: L.cf_compress_ablation(
+        mode, bits, 0, P(0x100000), P(ap) if ap else None, P(0x300000), P(0x400000),
+        P(0x500000), n, None)
+    assert call(0) == CF_E_ARG                 # mode 0 is cf_compress itself
+    assert call(3) == CF_E_ARG
+    assert call(1, bits=4) == CF_E_ARG
+    assert call(1, ap=0) == CF_E_NULL          # no-EF needs the previous activation
+    assert call(2, ap=0) == CF_E_DEVICE        # naive does not
+    assert call(1, n=100) == CF_E_SHAPE
+    assert call(1, ap=0x200008) == CF_E_ALIGN
+    assert call(1, ap=0x300000) == CF_E_ALIAS   # a_prev (input) overlapping ahat (output)
+    L.cf_decompress_bf16.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 4 + [ctypes.c_int64,
+                                                                               ctypes.c_void_p])
+    assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), None, 128, None) == CF_E_NULL
+    assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), P(0x40008), 128, None) == CF_E_ALIGN
+    assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), P(0x30000), 128, None) == CF_E_ALIAS
+    assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), P(0x40000), 128, None) == CF_E_DEVICE
