@@ -319,6 +319,8 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, w
         lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on)
     if on("compress2_cogvideo"):
         cogvideo_row(torch, np, cf, gen, dev, per_call, row)
+    if on("ef_study"):
+        rows["ef_study_flux_1bit"] = ef_study(torch, cf, wl, steps_d)
     torch.cuda.empty_cache()
     return rows
 
@@ -400,6 +402,41 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
                                                "hbm_frac": round(step_elems * 8 / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         del ahat, err, qs, ws, pay, rx
         torch.cuda.empty_cache()
+
+
+def ef_study(torch, cf, wl, steps_d):
+    """Error-feedback study on the FLUX trajectory (all tensors, Compact-1bit): the
+    relative error ||A_t - Ahat_t|| / ||A_t - A_{t-1}|| with error feedback, without it
+    (quantized raw step deltas), and for naive 1-bit of the whole activation."""
+    n = wl.slots * wl.numel
+    dev = steps_d[0].device
+    ef = cf.SenderState.create(n, dev)
+    cf.init_state(steps_d[0], ef.ahat, ef.err)
+    mirror = torch.empty(n, dtype=torch.float32, device=dev)
+    cf.init_state(steps_d[0], mirror)
+    naive = torch.empty(n, dtype=torch.float32, device=dev)
+    codes = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 128, dtype=torch.float32, device=dev)
+    out = {"steps": [], "ef": [], "no_ef": [], "naive": []}
+    for t in range(1, len(steps_d)):
+        a = steps_d[t].reshape(-1)
+        cf.compress(1, a, ef.ahat, ef.err, codes, scales)
+        cf.compress_ablation(cf.CF_MODE_NOEF, 1, a, mirror, a_prev=steps_d[t - 1].reshape(-1),
+                             codes=codes, scales=scales)
+        cf.compress_ablation(cf.CF_MODE_NAIVE, 1, a, naive, codes=codes, scales=scales)
+        if t in (1, 2, 4, 8, 16, len(steps_d) - 1):
+            a32 = a.float()
+            step = torch.linalg.norm(a32 - steps_d[t - 1].reshape(-1).float()).item()
+            out["steps"].append(t)
+            out["ef"].append(round(torch.linalg.norm(a32 - ef.ahat).item() / step, 4))
+            out["no_ef"].append(round(torch.linalg.norm(a32 - mirror).item() / step, 4))
+            out["naive"].append(round(torch.linalg.norm(a32 - naive).item() / step, 4))
+            del a32
+    log(f"ef_study: ||A-Ahat||/||dA|| at steps {out['steps']}: EF {out['ef']}, "
+        f"no EF {out['no_ef']}, naive {out['naive']}")
+    del ef, mirror, naive
+    torch.cuda.empty_cache()
+    return out
 
 
 def cogvideo_row(torch, np, cf, gen, dev, per_call, row):
