@@ -154,6 +154,9 @@ def lowrank_payload(m, n, rank, factor_bits):
     if factor_bits == 4:
         return (np.zeros(m * rank // 2, np.uint8), np.zeros(rank, np.float32),
                 np.zeros(n * rank // 2, np.uint8), np.zeros(rank, np.float32))
+    if factor_bits == 16:
+        return (np.zeros((m, rank), np.uint16), np.zeros(rank, np.float32),
+                np.zeros((n, rank), np.uint16), np.zeros(rank, np.float32))
     return (np.zeros((m, rank), np.float32), np.zeros(rank, np.float32),
             np.zeros((n, rank), np.float32), np.zeros(rank, np.float32))
 

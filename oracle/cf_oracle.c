@@ -36,7 +36,8 @@
  *     |R_jj| <= 1e-12 ||Y||_F set to zero), Q = r^T P, repeated `iters` times;
  *     INT4 factors use per-column absmax scales s = max|x| / 7 and codes
  *     rint(x / s) clamped to [-7, 7], two's-complement nibbles, low nibble
- *     first along the rank index.
+ *     first along the rank index; 16-bit factors (the table's "Pure Lowrank")
+ *     are the round-to-nearest-even bf16 of each fp32 factor element.
  * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 operation
  * rounds once, in the order written.
  */
@@ -59,6 +60,20 @@ static float act(int dtype, const void* a, int64_t i) {
     uint32_t bits = (uint32_t)((const uint16_t*)a)[i] << 16;
     float f;
     memcpy(&f, &bits, 4);
+    return f;
+}
+
+/* Round-to-nearest-even bf16 of a finite float, and its exact widening. */
+static uint16_t bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+static float bf16_widen(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
     return f;
 }
 
@@ -343,7 +358,8 @@ static int householder_orth(const double* Y, int64_t m, int k, double* P, int* a
  * Sender, low rank.  a: m x n activation; ahat, err: m x n fp32;
  * q_state: n x rank fp32 (in: start basis, out: last unquantized Q);
  * factor_bits 4: u = m*rank/2 bytes, v = n*rank/2 bytes of nibbles, scales
- * rank floats each; factor_bits 32: u, v fp32 (m x rank, n x rank), scales unused.
+ * rank floats each; factor_bits 16: u, v bf16 bits (m x rank, n x rank);
+ * factor_bits 32: u, v fp32 (m x rank, n x rank); scales unused unless 4.
  * Steps: r = a - Ahat; repeat iters times { Y = r Q; P = orth(Y); Q = r^T P;
  * round P, Q to fp32 }; quantize factors; R = P^ Q^^T; Ahat += R; e = a - Ahat.
  * A column that the QR guard zeroes keeps its previous start vector in q_state.
@@ -354,7 +370,7 @@ int cfo_lowrank_compress(int dtype, const void* a, float* ahat, float* err, int6
     if (!a || !ahat || !err || !q_state || !u || !v) return CFO_EARG;
     if (dtype != CFO_BF16 && dtype != CFO_F32) return CFO_EARG;
     if (m <= 0 || n <= 0 || rank < 1 || rank > (m < n ? m : n) || iters < 1) return CFO_EARG;
-    if (factor_bits != 4 && factor_bits != 32) return CFO_EARG;
+    if (factor_bits != 4 && factor_bits != 16 && factor_bits != 32) return CFO_EARG;
     if (factor_bits == 4 && ((rank & 1) || !u_scales || !v_scales)) return CFO_EARG;
     const int k = rank;
     int rc = CFO_ENOMEM;
@@ -396,6 +412,15 @@ int cfo_lowrank_compress(int dtype, const void* a, float* ahat, float* err, int6
         if (cfo_int4_quantize(Qf, n, k, (uint8_t*)v, v_scales)) goto done;
         cfo_int4_dequantize((const uint8_t*)u, u_scales, m, k, Uh);
         cfo_int4_dequantize((const uint8_t*)v, v_scales, n, k, Vh);
+    } else if (factor_bits == 16) {
+        for (int64_t i = 0; i < m * k; ++i) {
+            ((uint16_t*)u)[i] = bf16_rne(Pf[i]);
+            Uh[i] = bf16_widen(((uint16_t*)u)[i]);
+        }
+        for (int64_t i = 0; i < n * k; ++i) {
+            ((uint16_t*)v)[i] = bf16_rne(Qf[i]);
+            Vh[i] = bf16_widen(((uint16_t*)v)[i]);
+        }
     } else {
         memcpy(u, Pf, sizeof(float) * (size_t)(m * k));
         memcpy(v, Qf, sizeof(float) * (size_t)(n * k));
@@ -422,7 +447,7 @@ done:
 int cfo_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
                            const float* v_scales, float* ahat, int64_t m, int64_t n, int rank) {
     if (!u || !v || !ahat || m <= 0 || n <= 0 || rank < 1) return CFO_EARG;
-    if (factor_bits != 4 && factor_bits != 32) return CFO_EARG;
+    if (factor_bits != 4 && factor_bits != 16 && factor_bits != 32) return CFO_EARG;
     if (factor_bits == 4 && ((rank & 1) || !u_scales || !v_scales)) return CFO_EARG;
     const int k = rank;
     float* Uh = (float*)malloc(sizeof(float) * (size_t)(m * k));
@@ -431,6 +456,9 @@ int cfo_lowrank_decompress(int factor_bits, const void* u, const float* u_scales
     if (factor_bits == 4) {
         cfo_int4_dequantize((const uint8_t*)u, u_scales, m, k, Uh);
         cfo_int4_dequantize((const uint8_t*)v, v_scales, n, k, Vh);
+    } else if (factor_bits == 16) {
+        for (int64_t i = 0; i < m * k; ++i) Uh[i] = bf16_widen(((const uint16_t*)u)[i]);
+        for (int64_t i = 0; i < n * k; ++i) Vh[i] = bf16_widen(((const uint16_t*)v)[i]);
     } else {
         memcpy(Uh, u, sizeof(float) * (size_t)(m * k));
         memcpy(Vh, v, sizeof(float) * (size_t)(n * k));

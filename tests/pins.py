@@ -446,6 +446,34 @@ def pin_lowrank_receiver(O):
             assert np.array_equal(er, (f32(traj[t]) - ah).astype(np.float32))
 
 
+def pin_bf16_factors(O):
+    """16-bit factors ("Pure Lowrank"): each factor element is the round-to-nearest-even
+    bf16 of the fp32 factor (checked by brute force over the neighbouring bf16 values,
+    ties to the even mantissa), and the reconstruction uses exactly those values."""
+    rng = np.random.default_rng(11)
+    m, n, k = 64, 96, 8
+    a = rng.standard_normal((m, n)).astype(np.float32)
+    q0 = rng.standard_normal((n, k)).astype(np.float32)
+    ah32, e32, q32 = np.zeros_like(a), np.zeros_like(a), q0.copy()
+    u32, _, v32, _ = O.lowrank_compress(a, ah32, e32, q32, k, 2, 32)
+    ah16, e16, q16 = np.zeros_like(a), np.zeros_like(a), q0.copy()
+    u16, _, v16, _ = O.lowrank_compress(a, ah16, e16, q16, k, 2, 16)
+    assert np.array_equal(q16, q32), "the iteration does not depend on the factor format"
+    for x32, x16 in ((u32, u16), (v32, v16)):
+        x = x32.reshape(-1).astype(np.float32)
+        hi = x.view(np.uint32) >> 16
+        cand = np.stack([hi, hi + 1]).astype(np.uint32)         # truncation and the next value up
+        vals = (cand << 16).view(np.float32).astype(np.float64)
+        d = np.abs(vals - x.astype(np.float64))
+        pick = np.where(d[0] < d[1], cand[0], np.where(d[1] < d[0], cand[1],
+                        np.where(cand[0] % 2 == 0, cand[0], cand[1])))
+        assert np.array_equal(x16.reshape(-1).astype(np.uint32), pick)
+    uh = (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vh = (v16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want = (uh @ vh.T).astype(np.float32)
+    assert np.array_equal(ah16, (np.zeros_like(a) + want).astype(np.float32))
+
+
 def pin_payload_size(O=None):
     """Rank-32 INT4 payload of a 1024 x 3072 bf16 tensor: about 100x smaller
     (Key results: 'about 100x compression (rank-32 INT4)')."""
@@ -456,6 +484,8 @@ def pin_payload_size(O=None):
     assert payload == 65792
     ratio = m * n * 2 / payload
     assert 90 < ratio < 110, ratio
+    # rank 8 with 16-bit factors spends the same budget ("Pure Lowrank" row of the table)
+    assert (m + n) * 8 * 2 == 65536
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

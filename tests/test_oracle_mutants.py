@@ -68,9 +68,11 @@ MUTANTS = [
     ("lowrank_single_iteration", "for (int it = 0; it < iters; ++it) {",
      "for (int it = 0; it < 1; ++it) {"),
     ("lowrank_receiver_dequant_v",
-     "cfo_int4_dequantize((const uint8_t*)v, v_scales, n, k, Vh);\n    } else {\n        memcpy(Uh, u,",
-     "cfo_int4_dequantize((const uint8_t*)v, u_scales, n, k, Vh);\n    } else {\n        memcpy(Uh, u,"),
+     "cfo_int4_dequantize((const uint8_t*)v, v_scales, n, k, Vh);\n    } else if (factor_bits == 16) {\n        for (int64_t i = 0; i < m * k; ++i) Uh[i] = bf16_widen",
+     "cfo_int4_dequantize((const uint8_t*)v, u_scales, n, k, Vh);\n    } else if (factor_bits == 16) {\n        for (int64_t i = 0; i < m * k; ++i) Uh[i] = bf16_widen"),
     ("explicit_ef_error_sign", "err[base + i] = r[i] - d[i];", "err[base + i] = d[i] - r[i];"),
+    ("bf16_truncates", "return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);",
+     "return (uint16_t)(u >> 16);"),
 ]
 
 
