@@ -268,8 +268,9 @@ def lowrank_payload(batch: int, m: int, n: int, rank: int, factor_bits: int, dev
                 torch.empty(batch * rank, dtype=torch.float32, device=device),
                 torch.empty(batch * n * rank // 2, dtype=torch.uint8, device=device),
                 torch.empty(batch * rank, dtype=torch.float32, device=device))
-    return (torch.empty(batch * m * rank, dtype=torch.float32, device=device), None,
-            torch.empty(batch * n * rank, dtype=torch.float32, device=device), None)
+    dt = torch.int16 if factor_bits == 16 else torch.float32  # bf16 bits or fp32
+    return (torch.empty(batch * m * rank, dtype=dt, device=device), None,
+            torch.empty(batch * n * rank, dtype=dt, device=device), None)
 
 
 def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,

@@ -198,7 +198,7 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
                         float* u_scales, void* v, float* v_scales, void* workspace, size_t ws_bytes,
                         void* stream) {
     if (a_dtype != CF_BF16 && a_dtype != CF_F32) return CF_E_ARG;
-    if (factor_bits != 4 && factor_bits != 32) return CF_E_ARG;
+    if (factor_bits != 4 && factor_bits != 16 && factor_bits != 32) return CF_E_ARG;
     if (iters < 1 || iters > 64) return CF_E_ARG;
     if (!a || !ahat || !err || !q_state || !u || !v || !workspace) return CF_E_NULL;
     if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
@@ -210,7 +210,7 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
         return CF_E_ALIGN;
     if (ws_bytes < need) return CF_E_WORKSPACE;
     const int64_t numel = m * n * batch;
-    const int64_t fsz = factor_bits == 4 ? 1 : 8;  // factor bytes per (row, rank) pair, times 2
+    const int64_t fsz = factor_bits / 4;  // factor bytes per (row, rank) pair, times 2
     const Range r[8] = {range_of(a, act_bytes(a_dtype, numel)),
                         range_of(ahat, numel * 4),
                         range_of(err, numel * 4),
@@ -235,7 +235,7 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
 int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
                           const float* v_scales, float* ahat, int64_t m, int64_t n, int rank,
                           int batch, void* stream) {
-    if (factor_bits != 4 && factor_bits != 32) return CF_E_ARG;
+    if (factor_bits != 4 && factor_bits != 16 && factor_bits != 32) return CF_E_ARG;
     if (!u || !v || !ahat) return CF_E_NULL;
     if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
     if (cf_lowrank_workspace_bytes(m, n, rank, batch) == 0 || (factor_bits == 4 && (rank & 1)))
@@ -244,7 +244,7 @@ int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales,
         (v_scales && !aligned4(v_scales)))
         return CF_E_ALIGN;
     const int64_t numel = m * n * batch;
-    const int64_t fsz = factor_bits == 4 ? 1 : 8;
+    const int64_t fsz = factor_bits / 4;
     const Range r[5] = {range_of(ahat, numel * 4),
                         range_of(u, int64_t(batch) * m * rank * fsz / 2),
                         range_of(v, int64_t(batch) * n * rank * fsz / 2),

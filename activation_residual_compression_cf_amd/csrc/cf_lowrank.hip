@@ -11,7 +11,8 @@
 // Per tensor (m x n, row-major), with Q the n x k start basis:
 //   r = a - Ahat                                   (fp32, kept in the workspace)
 //   repeat iters times:  Y = r Q;  P = orth(Y);  Q = r^T P
-//   U^ = int4(P), V^ = int4(Q)  (per-column absmax / 7, round half even, [-7, 7])
+//   U^ = int4(P), V^ = int4(Q)  (per-column absmax / 7, round half even, [-7, 7]),
+//   or the bf16 of P and Q (16-bit factors), or P and Q themselves (fp32)
 //   Ahat = Ahat + U^ V^^T;   e = a - Ahat;   q_state = Q (warm start)
 // orth(Y) is the thin Q factor with diag(R) >= 0, computed as Cholesky QR with the
 // Gram matrix, the factorisation and the triangular solve in fp64 (fp32 Cholesky QR
@@ -25,11 +26,11 @@
 //   k_lr_project    Y partials = r Q over column segments; the first pass also forms
 //                   and stores r.  fp32 MFMA 16x16x4: a lane's float4 of r supplies
 //                   4 k-slices, Q^T float4s the matching B operands.
-//   k_lr_orth       one workgroup per tensor: Y = sum of partials (fixed order), fp64
+//   k_lr_gram, k_lr_chol, k_lr_solve  orth: Y = sum of partials (fixed order), fp64
 //                   Gram, Cholesky with the rank guard, P = Y R^-1.
 //   k_lr_backproject Q^T = P^T r, MFMA; the four waves of a workgroup split the rows
 //                   and their partials are summed in LDS in a fixed order.
-//   k_lr_quantize   INT4 (or fp32) factors, scales, and the q_state update.
+//   k_lr_colmax, k_lr_pack  INT4 (or bf16 / fp32) factors, scales, q_state update.
 //   k_lr_reconstruct Ahat += U^ V^^T (MFMA, factors dequantized on the fly from the
 //                   payload) and e = a - Ahat; the receiver runs the same kernel
 //                   without e, so both sides produce identical bits.
@@ -586,6 +587,26 @@ __global__ __launch_bounds__(256) void k_lr_pack(const float* __restrict__ p, co
                 for (int q = 0; q < k / 2; ++q) out[q] = static_cast<uint8_t>(words[q / 4] >> (8 * (q % 4)));
             }
         }
+    } else if (factor_bits == 16 && row < rows) {
+        // round-to-nearest-even bf16 of each element; 8-byte stores when k % 4 == 0
+        uint16_t* out = static_cast<uint16_t*>(f ? v : u) + (b * rows + row) * k;
+        auto rne = [](float xf) -> uint32_t {
+            const uint32_t w = __float_as_uint(xf);
+            return (w + 0x7FFFu + ((w >> 16) & 1u)) >> 16;
+        };
+        if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(f ? v : u) & 7) == 0) {
+#pragma unroll
+            for (int kk = 0; kk < kp; kk += 4) {
+                if (kk >= k) break;
+                const uint32_t lo = rne(factor_elem(x, f, n, kp, row, kk)) |
+                                    (rne(factor_elem(x, f, n, kp, row, kk + 1)) << 16);
+                const uint32_t hi = rne(factor_elem(x, f, n, kp, row, kk + 2)) |
+                                    (rne(factor_elem(x, f, n, kp, row, kk + 3)) << 16);
+                *reinterpret_cast<uint2*>(out + kk) = make_uint2(lo, hi);
+            }
+        } else {
+            for (int kk = 0; kk < k; ++kk) out[kk] = static_cast<uint16_t>(rne(factor_elem(x, f, n, kp, row, kk)));
+        }
     } else if (row < rows) {
         float* out = static_cast<float*>(f ? v : u) + (b * rows + row) * k;
         if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(f ? v : u) & 15) == 0) {
@@ -640,6 +661,8 @@ __device__ __forceinline__ float factor_at(const void* f, const float* scales, i
         const int nib = (kk & 1) ? (byte >> 4) : (byte & 0xF);
         const int c = nib >= 8 ? nib - 16 : nib;
         return static_cast<float>(c) * scales[kk];
+    } else if constexpr (FB == 16) {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(f)[row * k + kk]) << 16);
     } else {
         return static_cast<const float*>(f)[row * k + kk];
     }
@@ -666,8 +689,8 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int li = lane & 15, lg = lane >> 4;
 
-    const int64_t usz = FB == 4 ? m * k / 2 : m * k * 4;  // bytes per tensor
-    const int64_t vsz = FB == 4 ? n * k / 2 : n * k * 4;
+    const int64_t usz = m * k * FB / 8;  // bytes per tensor
+    const int64_t vsz = n * k * FB / 8;
     const void* ub = static_cast<const uint8_t*>(u) + b * usz;
     const void* vb = static_cast<const uint8_t*>(v) + b * vsz;
     const float* usb = FB == 4 ? u_scales + b * k : nullptr;
@@ -759,8 +782,9 @@ hipError_t launch_reconstruct_fb(int k, int64_t total, void** args, hipStream_t 
 
 template <bool HAS_E, typename ActT>
 hipError_t launch_reconstruct(int factor_bits, int k, int64_t total, void** args, hipStream_t stream) {
-    return factor_bits == 4 ? launch_reconstruct_fb<HAS_E, ActT, 4>(k, total, args, stream)
-                            : launch_reconstruct_fb<HAS_E, ActT, 32>(k, total, args, stream);
+    if (factor_bits == 4) return launch_reconstruct_fb<HAS_E, ActT, 4>(k, total, args, stream);
+    if (factor_bits == 16) return launch_reconstruct_fb<HAS_E, ActT, 16>(k, total, args, stream);
+    return launch_reconstruct_fb<HAS_E, ActT, 32>(k, total, args, stream);
 }
 
 template <typename ActT, int KT>

@@ -321,6 +321,8 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, w
         cogvideo_row(torch, np, cf, gen, dev, per_call, row)
     if on("ef_study"):
         rows["ef_study_flux_1bit"] = ef_study(torch, cf, wl, steps_d)
+    if on("lowrank_study"):
+        rows["lowrank_study_flux"] = lowrank_study(torch, np, cf, gen, wl, steps_d)
     torch.cuda.empty_cache()
     return rows
 
@@ -436,6 +438,58 @@ def ef_study(torch, cf, wl, steps_d):
         f"no EF {out['no_ef']}, naive {out['naive']}")
     del ef, mirror, naive
     torch.cuda.empty_cache()
+    return out
+
+
+def lowrank_study(torch, np, cf, gen, wl, steps_d, nslots=16):
+    """Low-rank variants on the first `nslots` FLUX tensors over the whole trajectory:
+    final ||A - Ahat|| / ||A||, payload bytes per tensor and time per call (all 114
+    tensors) for rank 32 INT4 (Compact-Lowrank) and rank 8 bf16 ("Pure Lowrank") at 2
+    and 10 iterations, warm-started from the previous step's Q or cold (a fresh
+    random basis every step)."""
+    dev = steps_d[0].device
+    arms = [("r32_q2_int4_warm", 32, 2, 4, True), ("r8_q2_bf16_warm", 8, 2, 16, True),
+            ("r8_q10_bf16_warm", 8, 10, 16, True), ("r8_q2_bf16_cold", 8, 2, 16, False)]
+    out = {}
+    for name, rank, iters, fb, warm in arms:
+        ahat = torch.empty((nslots, wl.m, wl.n), dtype=torch.float32, device=dev)
+        err = torch.empty_like(ahat)
+        a = [s.reshape(wl.slots, wl.m, wl.n)[:nslots] for s in steps_d]
+        cf.init_state(a[0], ahat, err)
+        basis = lambda seed: torch.from_numpy(np.stack([gen.start_basis(seed, s, wl.n, rank)
+                                                        for s in range(nslots)])).to(dev)
+        qs = basis(0)
+        ws = torch.empty(cf.lowrank_workspace_bytes(wl.m, wl.n, rank, nslots), dtype=torch.uint8,
+                         device=dev)
+        for t in range(1, len(a)):
+            if not warm:
+                qs = basis(t)
+            cf.lowrank_compress(a[t], ahat, err, qs, rank, iters, fb, workspace=ws)
+        a32 = a[-1].float()
+        rel = (torch.linalg.norm(a32 - ahat) / torch.linalg.norm(a32)).item()
+        payload = (wl.m + wl.n) * rank * fb // 8 + (8 * rank if fb == 4 else 0)
+        out[name] = {"final_rel_err": round(rel, 5), "payload_bytes": payload,
+                     "ratio": round(wl.numel * 2 / payload, 1)}
+        del ahat, err, a32, ws
+    # time per call over all tensors for the 16-bit arms (the INT4 arm is timed in its row)
+    for name, rank, iters, fb, warm in arms[1:3]:
+        ahat = torch.empty((wl.slots, wl.m, wl.n), dtype=torch.float32, device=dev)
+        err = torch.empty_like(ahat)
+        cf.init_state(steps_d[0], ahat, err)
+        qs = torch.from_numpy(np.stack([gen.start_basis(0, s, wl.n, rank)
+                                        for s in range(wl.slots)])).to(dev)
+        ws = torch.empty(cf.lowrank_workspace_bytes(wl.m, wl.n, rank, wl.slots), dtype=torch.uint8,
+                         device=dev)
+        pay = cf.lowrank_payload(wl.slots, wl.m, wl.n, rank, fb, dev)
+        a3 = [x.view(wl.slots, wl.m, wl.n) for x in steps_d[1:]]
+        cf.lowrank_compress(a3[0], ahat, err, qs, rank, iters, fb, pay, ws)
+        it = iter(range(10 ** 9))
+        ms = time_calls(torch, lambda: cf.lowrank_compress(a3[1 + next(it) % (len(a3) - 1)], ahat, err,
+                                                           qs, rank, iters, fb, pay, ws), 4)
+        out[name]["ms_per_step_114"] = round(ms, 4)
+        del ahat, err, qs, ws, pay
+    torch.cuda.empty_cache()
+    log("lowrank_study: " + ", ".join(f"{k} err {v['final_rel_err']} ({v['ratio']}x)" for k, v in out.items()))
     return out
 
 

@@ -144,6 +144,8 @@ int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const v
  *   factor_bits 4:  U = int4(P), V = int4(Q): per column j, s_j = max|x| / 7,
  *     code = rint(x / s_j) clamped to [-7, 7] (0 when s_j = 0), two's-complement
  *     nibbles, row-major rows x rank, low nibble first;  U^ = code * s_j;
+ *   factor_bits 16: U, V = the round-to-nearest-even bf16 of P, Q, row-major
+ *     (rows x rank) (the table's "Pure Lowrank" variant); scales unused;
  *   factor_bits 32: U = P, V = Q as fp32 row-major (rows x rank); scales unused;
  *   ahat = ahat + U^ V^^T;   err = a - ahat;
  *   q_state = Q (a column zeroed by the rank guard keeps its previous value).
@@ -151,9 +153,9 @@ int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const v
  *   a: batch*m*n (a_dtype), in; ahat: batch*m*n fp32, in/out; err: out;
  *   q_state: batch*n*rank fp32, in/out (the start basis; a seeded N(0,1) matrix
  *     before the first compressed step);
- *   u: batch*m*rank/2 bytes (4) or batch*m*rank fp32 (32), out;
- *   v: batch*n*rank/2 bytes (4) or batch*n*rank fp32 (32), out;
- *   u_scales, v_scales: batch*rank fp32, out (may be NULL when factor_bits = 32);
+ *   u: batch*m*rank*factor_bits/8 bytes, out; v: batch*n*rank*factor_bits/8 bytes,
+ *     out; both 4-byte aligned;
+ *   u_scales, v_scales: batch*rank fp32, out (may be NULL unless factor_bits = 4);
  *   workspace: ws_bytes >= cf_lowrank_workspace_bytes(m, n, rank, batch), 256-byte
  *     aligned; scratch, its contents are not preserved between calls.
  * Limits: m and n positive multiples of 16; 1 <= rank <= min(m, n, 64); rank even
