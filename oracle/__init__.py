@@ -8,8 +8,9 @@ and the two share no code.
 Every function follows "Accelerating Parallel Diffusion Model Serving with Residual
 Compression" (CompactFusion summary), section Approach (residual against the previous
 reconstruction, sender-side error feedback, low rank with INT4 factors) and its
-measured-effects table (1-bit / 2-bit variants, warmup, rank 32, iterations); the
-readings the pages leave open are listed at the top of ``cf_oracle.c``.
+measured-effects table (1-bit / 2-bit variants, warmup, rank 32, iterations), and the
+Limitations list, which names sparsity as the other fast compressor family (read here as
+per-group top-k of the residual with the same error feedback); the readings the pages leave open are listed at the top of ``cf_oracle.c``.
 
 Activations are numpy arrays: ``uint16`` holds raw bf16 bits, ``float32`` is fp32.
 State arrays (``ahat``, ``err``) are float32 and updated in place.
@@ -37,6 +38,8 @@ _SIG = {
     "cfo_int4_dequantize": "pplip",
     "cfo_lowrank_compress": "ippplliiippppp",
     "cfo_lowrank_decompress": "ippppplli",
+    "cfo_topk_compress": "iipppppl",
+    "cfo_topk_decompress": "ipppl",
 }
 _CT = {"i": ctypes.c_int, "l": ctypes.c_int64, "p": ctypes.c_void_p}
 
@@ -147,6 +150,19 @@ class Oracle:
         m, n = ahat.shape
         _check(self.L.cfo_lowrank_decompress(factor_bits, _p(u), _p(us), _p(v), _p(vs), _p(ahat),
                                              m, n, rank), "lowrank_decompress")
+
+    def topk_compress(self, k, a, ahat, err):
+        """One top-k sender step; returns (idx uint8[G*k], vals uint16 bf16 bits[G*k])."""
+        n = a.size
+        idx = np.zeros(n // GROUP * k, np.uint8)
+        vals = np.zeros(n // GROUP * k, np.uint16)
+        _check(self.L.cfo_topk_compress(k, _dtype_code(a), _p(a), _p(ahat), _p(err), _p(idx),
+                                        _p(vals), n), "topk_compress")
+        return idx, vals
+
+    def topk_decompress(self, k, idx, vals, ahat):
+        _check(self.L.cfo_topk_decompress(k, _p(idx), _p(vals), _p(ahat), ahat.size),
+               "topk_decompress")
 
 
 def lowrank_payload(m, n, rank, factor_bits):

@@ -37,7 +37,10 @@
  *     INT4 factors use per-column absmax scales s = max|x| / 7 and codes
  *     rint(x / s) clamped to [-7, 7], two's-complement nibbles, low nibble
  *     first along the rank index; 16-bit factors (the table's "Pure Lowrank")
- *     are the round-to-nearest-even bf16 of each fp32 factor element.
+ *     are the round-to-nearest-even bf16 of each fp32 factor element;
+ *   - top-k sparsity (named only as a compressor family): per group of 128 the
+ *     k residuals of largest |r| (ties to the lower index), sent as index bytes
+ *     and bf16 values in increasing index order, with the same error feedback.
  * Built with -O2 -ffp-contract=off and no fast-math, so every fp32 operation
  * rounds once, in the order written.
  */
@@ -470,5 +473,79 @@ int cfo_lowrank_decompress(int factor_bits, const void* u, const float* u_scales
             ahat[i * n + l] = ahat[i * n + l] + (float)s;
         }
     free(Uh); free(Vh);
+    return CFO_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Top-k sparsification of the residual (Limitations: quantization and
+ * sparsity are the fast compressor families the low-rank variant is compared
+ * with; the pages define no sparsity rule, so this reading is taken).  Per
+ * group of 128: keep the k residuals of largest |r|, ordered by the bit pattern
+ * of |r| (the magnitude order for non-NaN values), equal magnitudes going to
+ * the lower index; the kept entries are written in increasing index order as
+ * one index byte (0..127) and the round-to-nearest-even bf16 of r.  Error
+ * feedback as for the quantizers: Ahat += widened value at the kept indices,
+ * e = a - Ahat everywhere (so the dropped residuals stay in e).
+ * Payload per group: k index bytes at idx[g*k ..], k bf16 values at vals[g*k ..].
+ * ------------------------------------------------------------------------- */
+static uint32_t mag_key(float r) {
+    float m = fabsf(r);
+    uint32_t u;
+    memcpy(&u, &m, 4);
+    return u;
+}
+
+static const float* g_sort_r; /* the group being sorted (comparators take no context) */
+
+static int by_magnitude(const void* x, const void* y) {
+    int i = *(const int*)x, j = *(const int*)y;
+    uint32_t ki = mag_key(g_sort_r[i]), kj = mag_key(g_sort_r[j]);
+    if (ki != kj) return ki > kj ? -1 : 1;
+    return i < j ? -1 : (i > j);
+}
+
+static int by_index(const void* x, const void* y) {
+    int i = *(const int*)x, j = *(const int*)y;
+    return i < j ? -1 : (i > j);
+}
+
+int cfo_topk_compress(int k, int dtype, const void* a, float* ahat, float* err, uint8_t* idx,
+                      uint16_t* vals, int64_t numel) {
+    if (k < 1 || k > CFO_GROUP || check_common(1, dtype, numel) || !a || !ahat || !err || !idx ||
+        !vals)
+        return CFO_EARG;
+    float r[CFO_GROUP];
+    int order[CFO_GROUP];
+    for (int64_t g = 0; g < numel / CFO_GROUP; ++g) {
+        int64_t base = g * CFO_GROUP;
+        for (int i = 0; i < CFO_GROUP; ++i) {
+            r[i] = act(dtype, a, base + i) - ahat[base + i];
+            order[i] = i;
+        }
+        g_sort_r = r;
+        qsort(order, CFO_GROUP, sizeof(int), by_magnitude);
+        qsort(order, (size_t)k, sizeof(int), by_index);
+        for (int j = 0; j < k; ++j) {
+            int i = order[j];
+            uint16_t h = bf16_rne(r[i]);
+            idx[g * k + j] = (uint8_t)i;
+            vals[g * k + j] = h;
+            ahat[base + i] = ahat[base + i] + bf16_widen(h);
+        }
+        for (int i = 0; i < CFO_GROUP; ++i) err[base + i] = act(dtype, a, base + i) - ahat[base + i];
+    }
+    return CFO_OK;
+}
+
+/* Receiver: the same widened values added at the sent indices (low 7 bits of
+ * each index byte, so any payload stays inside its group). */
+int cfo_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* ahat, int64_t numel) {
+    if (k < 1 || k > CFO_GROUP || check_common(1, CFO_F32, numel) || !idx || !vals || !ahat)
+        return CFO_EARG;
+    for (int64_t g = 0; g < numel / CFO_GROUP; ++g)
+        for (int j = 0; j < k; ++j) {
+            int64_t e = g * CFO_GROUP + (idx[g * k + j] & 127);
+            ahat[e] = ahat[e] + bf16_widen(vals[g * k + j]);
+        }
     return CFO_OK;
 }

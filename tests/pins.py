@@ -488,6 +488,187 @@ def pin_payload_size(O=None):
     assert (m + n) * 8 * 2 == 65536
 
 
+# ---------------------------------------------------------------- top-k sparsity
+# Reading of the sparsity compressor the pages name (Limitations): per group of 128
+# keep the k residuals of largest |r| (ties to the lower index), sent in increasing
+# index order as index bytes and bf16 values, with the same error feedback.
+def _bf16_widen(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def _assert_nearest_bf16(h: np.ndarray, r: np.ndarray):
+    """Each h is a nearest bf16 of r (neighbours one code up and down are no closer),
+    and an exact halfway case takes the even code."""
+    h = h.astype(np.int64)
+    r64 = r.astype(np.float64)
+    d0 = np.abs(_bf16_widen(h.astype(np.uint16)).astype(np.float64) - r64)
+    mag = h & 0x7FFF
+    sign = h & 0x8000
+    for step in (-1, 1):
+        nm = mag + step
+        ok = (nm >= 0) & (nm < 0x7F80)
+        nb = (sign | np.clip(nm, 0, 0x7F7F)).astype(np.uint16)
+        dn = np.abs(_bf16_widen(nb).astype(np.float64) - r64)
+        assert np.all(~ok | (d0 <= dn)), "value is not a nearest bf16"
+        tie = ok & (d0 == dn) & (d0 > 0)
+        assert np.all((h[tie] & 1) == 0), "halfway case not rounded to even"
+
+
+def _assert_topk_selection(r: np.ndarray, idx: np.ndarray, k: int):
+    """Per group: k strictly increasing indices; every kept |r| beats every dropped one,
+    or equals it at a lower index."""
+    G = r.size // 128
+    r = r.reshape(G, 128)
+    idx = idx.reshape(G, k).astype(np.int64)
+    assert np.all(idx < 128)
+    if k > 1:
+        assert np.all(np.diff(idx, axis=1) > 0), "indices not strictly increasing"
+    mag = np.abs(r.astype(np.float64))
+    kept = np.zeros((G, 128), bool)
+    np.put_along_axis(kept, idx, True, axis=1)
+    if k == 128:
+        return
+    kmin = np.where(kept, mag, np.inf).min(axis=1)
+    dmax = np.where(kept, -np.inf, mag).max(axis=1)
+    assert np.all(kmin >= dmax), "a dropped residual is larger than a kept one"
+    pos = np.arange(128)
+    last_kept_tie = np.where(kept & (mag == kmin[:, None]), pos, -1).max(axis=1)
+    first_drop_tie = np.where(~kept & (mag == dmax[:, None]), pos, 999).min(axis=1)
+    tied = kmin == dmax
+    assert np.all(~tied | (last_kept_tie < first_drop_tie)), "tie not broken to the lower index"
+
+
+def pin_golden_topk(O):
+    g = load_golden("topk_group.txt")
+    r = np.array([float(v) for v in g["r"]], np.float32)
+    for k in (3, 6):
+        a = np.zeros(128, np.float32)
+        a[: r.size] = r
+        ahat = np.zeros(128, np.float32)
+        err = np.zeros(128, np.float32)
+        idx, vals = O.topk_compress(k, a, ahat, err)
+        assert idx.tolist() == [int(v) for v in g[f"k{k}_idx"]], idx
+        assert vals.tolist() == [int(h, 16) for h in g[f"k{k}_vals_hex"]], [hex(v) for v in vals]
+        want = np.zeros(128, np.float32)
+        want[idx] = _bf16_widen(vals)
+        assert np.array_equal(ahat, want)
+        rx = np.zeros(128, np.float32)
+        O.topk_decompress(k, idx, vals, rx)
+        assert np.array_equal(rx, want)
+    for i, e in zip(g["k6_err_idx"], g["k6_err"]):
+        assert err[int(i)] == np.float32(float(e)), (i, err[int(i)])
+
+
+def pin_topk_selection_bruteforce(O):
+    """Selection and values against the definition, on groups full of ties (values on a
+    coarse grid, signed zeros, a denormal) and on FLUX-like residuals."""
+    rng = np.random.default_rng(11)
+    grid = rng.integers(-4, 5, size=64 * 128).astype(np.float32) * np.float32(0.75)
+    grid[5] = -0.0
+    grid[300] = np.float32(1e-40)
+    smooth = f32(scaled_trajectory(16, 512, 2)[1]) - f32(scaled_trajectory(16, 512, 2)[0])
+    for r in (grid, smooth.reshape(-1).astype(np.float32)):
+        for k in (1, 5, 12, 64, 127, 128):
+            a = r.copy()
+            ahat = np.zeros_like(a)
+            err = np.zeros_like(a)
+            idx, vals = O.topk_compress(k, a, ahat, err)
+            _assert_topk_selection(r, idx, k)
+            rows = np.repeat(np.arange(r.size // 128), k) * 128
+            _assert_nearest_bf16(vals, r[rows + idx.astype(np.int64)])
+
+
+def pin_topk_zero_residual(O):
+    """r = 0 everywhere: every magnitude ties, so the first k indices are sent with
+    value +0 and nothing changes."""
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal(8 * 128).astype(np.float32)
+    ahat = a.copy()
+    err = np.full_like(a, 5.0)
+    idx, vals = O.topk_compress(12, a, ahat, err)
+    assert np.array_equal(idx.reshape(8, 12), np.tile(np.arange(12, dtype=np.uint8), (8, 1)))
+    assert not vals.any()
+    assert np.array_equal(ahat, a) and not err.any()
+
+
+def pin_topk_all_kept(O):
+    """k = 128 sends every residual; what stays in e is the bf16 rounding of r."""
+    traj = scaled_trajectory(8, 512, 2)
+    a = traj[1]
+    ahat = f32(traj[0]).copy()
+    prev = ahat.copy()
+    err = np.zeros_like(ahat)
+    idx, vals = O.topk_compress(128, a, ahat, err)
+    assert np.array_equal(idx.reshape(-1, 128), np.tile(np.arange(128, dtype=np.uint8), (32, 1)))
+    r = (f32(a) - prev).astype(np.float32).reshape(-1)
+    assert np.all(np.abs(r - _bf16_widen(vals)) <= np.abs(r) * 2.0 ** -8)
+    assert np.linalg.norm(err) <= 2.0 ** -8 * np.linalg.norm(r) * 1.01
+
+
+def pin_topk_ef(O):
+    """Error feedback with top-k: untouched entries keep their reconstruction, kept ones
+    add the sent value, e = fl(a - Ahat); the error stays bounded over 27 steps and
+    falls as k grows (FLUX-like and Gaussian trajectories)."""
+    for traj in (tiny_trajectory(28), scaled_trajectory(64, 512, 28)):
+        last = []
+        for k in (6, 12, 32, 128):
+            ahat = f32(traj[0]).copy()
+            err = np.zeros_like(ahat)
+            ratios = []
+            for t in range(1, len(traj)):
+                a = traj[t]
+                prev = ahat.copy().reshape(-1)
+                idx, vals = O.topk_compress(k, a, ahat, err)
+                pos = np.repeat(np.arange(prev.size // 128), k) * 128 + idx.astype(np.int64)
+                want = prev.copy()
+                want[pos] = (prev[pos] + _bf16_widen(vals)).astype(np.float32)
+                assert np.array_equal(ahat.reshape(-1), want)
+                assert np.array_equal(err, (f32(a) - ahat).astype(np.float32))
+                step = np.linalg.norm(f32(a) - f32(traj[t - 1]))
+                ratios.append(np.linalg.norm(f32(a) - ahat) / step)
+            assert max(ratios) < 2.0, (k, max(ratios))
+            assert ratios[-1] <= 1.05 * max(ratios[-6:]), "error still growing"
+            last.append(ratios[-1])
+        assert last[0] > last[1] > last[2] > 100 * last[3], last
+
+
+def pin_topk_sender_receiver(O):
+    traj = scaled_trajectory(32, 512, 5)
+    ahat = f32(traj[0]).copy()
+    err = np.zeros_like(ahat)
+    rx = ahat.copy()
+    for t in range(1, 5):
+        idx, vals = O.topk_compress(12, traj[t], ahat, err)
+        O.topk_decompress(12, idx, vals, rx)
+        assert np.array_equal(rx, ahat)
+
+
+def pin_topk_scaling_negation(O):
+    """Scaling a and Ahat by 2^j keeps the indices and scales the sent values by 2^j;
+    negating them keeps the indices and flips the values' signs."""
+    traj = scaled_trajectory(8, 512, 2)
+    a, a0 = f32(traj[1]), f32(traj[0])
+    idx0, v0 = O.topk_compress(9, a.copy(), a0.copy(), np.zeros_like(a))
+    for j in (-3, 5):
+        f = np.float32(2.0 ** j)
+        idx, v = O.topk_compress(9, (a * f).astype(np.float32), (a0 * f).astype(np.float32),
+                                 np.zeros_like(a))
+        assert np.array_equal(idx, idx0)
+        assert np.array_equal(_bf16_widen(v), (_bf16_widen(v0) * f).astype(np.float32))
+    idx, v = O.topk_compress(9, -a, -a0, np.zeros_like(a))
+    assert np.array_equal(idx, idx0)
+    assert np.array_equal(_bf16_widen(v), -_bf16_widen(v0))
+
+
+def pin_topk_payload(O=None):
+    """k = 12 spends 36 bytes per 128-element group: the 2-bit budget (32 code bytes and
+    a 4-byte scale), 7.1x smaller than the bf16 group."""
+    k = 12
+    per_group = k * 1 + k * 2
+    assert per_group == 128 * 2 // 8 + 4 == 36
+    assert abs(256 / per_group - 7.11) < 0.01
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

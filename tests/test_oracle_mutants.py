@@ -21,8 +21,8 @@ PINS = os.path.join(ROOT, "tests", "pins.py")
 # (name, text in cf_oracle.c, replacement)
 MUTANTS = [
     ("ef_error_sign",
-     "err[base + i] = act(dtype, a, base + i) - ahat[base + i];",
-     "err[base + i] = ahat[base + i] - act(dtype, a, base + i);"),
+     "d[i];\n            err[base + i] = act(dtype, a, base + i) - ahat[base + i];",
+     "d[i];\n            err[base + i] = ahat[base + i] - act(dtype, a, base + i);"),
     ("update_sign",
      "ahat[base + i] = ahat[base + i] + d[i];\n            err[base + i] = act",
      "ahat[base + i] = ahat[base + i] - d[i];\n            err[base + i] = act"),
@@ -73,6 +73,22 @@ MUTANTS = [
     ("explicit_ef_error_sign", "err[base + i] = r[i] - d[i];", "err[base + i] = d[i] - r[i];"),
     ("bf16_truncates", "return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);",
      "return (uint16_t)(u >> 16);"),
+    ("topk_ties_to_higher_index", "return i < j ? -1 : (i > j);\n}\n\nstatic int by_index",
+     "return i > j ? -1 : (i < j);\n}\n\nstatic int by_index"),
+    ("topk_keeps_smallest", "if (ki != kj) return ki > kj ? -1 : 1;",
+     "if (ki != kj) return ki < kj ? -1 : 1;"),
+    ("topk_signed_key", "float m = fabsf(r);", "float m = r;"),
+    ("topk_output_unsorted", "qsort(order, (size_t)k, sizeof(int), by_index);", "(void)by_index;"),
+    ("topk_value_truncated", "uint16_t h = bf16_rne(r[i]);",
+     "uint16_t h = (uint16_t)(mag_key(r[i]) >> 16) | (r[i] < 0.0f ? 0x8000u : 0u);"),
+    ("topk_one_slot_short", "for (int j = 0; j < k; ++j) {\n            int i = order[j];",
+     "for (int j = 0; j < k - 1; ++j) {\n            int i = order[j];"),
+    ("topk_sender_unrounded", "ahat[base + i] = ahat[base + i] + bf16_widen(h);",
+     "ahat[base + i] = ahat[base + i] + r[i];"),
+    ("topk_decode_slot_as_index", "int64_t e = g * CFO_GROUP + (idx[g * k + j] & 127);",
+     "int64_t e = g * CFO_GROUP + j;"),
+    ("topk_decode_group_stride", "int64_t e = g * CFO_GROUP + (idx[g * k + j] & 127);",
+     "int64_t e = g * k + (idx[g * k + j] & 127);"),
 ]
 
 
