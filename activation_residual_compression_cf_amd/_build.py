@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libcf.so")
-SOURCES = ["csrc/cf_api.hip", "csrc/cf_quant.hip", "csrc/cf_lowrank.hip"]
+SOURCES = ["csrc/cf_api.hip", "csrc/cf_quant.hip", "csrc/cf_lowrank.hip", "csrc/cf_topk.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -30,6 +30,8 @@ _SIG = {
     "cf_decompress": ("i", "ippplp"),
     "cf_decompress_bf16": ("i", "ipppplp"),
     "cf_compress_ablation": ("i", "iiipppppl" "p"),
+    "cf_topk_compress": ("i", "iippppplp"),
+    "cf_topk_decompress": ("i", "ippplp"),
     "cf_lowrank_compress": ("i", "ipppllii" "iipppppp" "zp"),
     "cf_lowrank_decompress": ("i", "ipppp" "pllii" "p"),
     "cf_lowrank_workspace_bytes": ("z", "llii"),
@@ -171,6 +173,24 @@ def compress_ablation(mode: int, bits: int, a: torch.Tensor, ahat: torch.Tensor,
         mode, bits, _act_dtype(a), _ptr(a), _ptr(a_prev), _ptr(ahat), _ptr(codes), _ptr(scales), n,
         _stream(stream)))
     return codes, scales
+
+
+def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
+                  idx: torch.Tensor | None = None, vals: torch.Tensor | None = None, stream=None):
+    """One top-k sender step; returns (idx uint8[numel/128*k], vals bf16 bits int16[numel/128*k])."""
+    slots = max(a.numel() // GROUP * k, 0)
+    if idx is None:
+        idx = torch.empty(slots, dtype=torch.uint8, device=a.device)
+    if vals is None:
+        vals = torch.empty(slots, dtype=torch.int16, device=a.device)
+    _check("cf_topk_compress", lib.cf_topk_compress(k, _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
+                                                    _ptr(idx), _ptr(vals), a.numel(), _stream(stream)))
+    return idx, vals
+
+
+def topk_decompress(k: int, idx: torch.Tensor, vals: torch.Tensor, ahat: torch.Tensor, stream=None):
+    _check("cf_topk_decompress", lib.cf_topk_decompress(k, _ptr(idx), _ptr(vals), _ptr(ahat), ahat.numel(),
+                                                        _stream(stream)))
 
 
 def _dev_ptr(t: torch.Tensor) -> int:

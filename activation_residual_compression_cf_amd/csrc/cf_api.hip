@@ -78,7 +78,7 @@ const char* cf_strerror(int status) {
         case CF_E_NULL: return "required pointer is NULL";
         case CF_E_SHAPE: return "size out of range (numel must be a positive multiple of 128)";
         case CF_E_ALIGN: return "pointer misaligned (16 bytes; scales 4 bytes)";
-        case CF_E_ARG: return "unsupported bits, dtype or mode";
+        case CF_E_ARG: return "unsupported bits, k, dtype or mode";
         case CF_E_ALIAS: return "output range overlaps another operand";
         case CF_E_WORKSPACE: return "workspace missing or too small";
         case CF_E_DEVICE: return "current device is not gfx950";
@@ -180,6 +180,41 @@ int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const v
     if (int rc = check_device()) return rc;
     return cf::launch_compress_ablation(mode, bits, a_dtype, a, a_prev, ahat, codes, scales, numel,
                                         static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
+int cf_topk_compress(int k, int a_dtype, const void* a, float* ahat, float* err, uint8_t* idx, uint16_t* vals,
+                     int64_t numel, void* stream) {
+    if (k < 1 || k > CF_GROUP || (a_dtype != CF_BF16 && a_dtype != CF_F32)) return CF_E_ARG;
+    if (!a || !ahat || !err || !idx || !vals) return CF_E_NULL;
+    if (int rc = valid_numel(numel)) return rc;
+    if (!aligned16(a) || !aligned16(ahat) || !aligned16(err) || (reinterpret_cast<uintptr_t>(vals) & 1u))
+        return CF_E_ALIGN;
+    const int64_t slots = numel / CF_GROUP * k;
+    const Range r[5] = {range_of(a, act_bytes(a_dtype, numel)), range_of(ahat, numel * 4),
+                        range_of(err, numel * 4), range_of(idx, slots), range_of(vals, slots * 2)};
+    const bool out[5] = {false, true, true, true, true};
+    if (any_alias(r, out)) return CF_E_ALIAS;
+    if (int rc = check_device()) return rc;
+    return cf::launch_topk_compress(k, a_dtype, a, ahat, err, idx, vals, numel,
+                                    static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
+int cf_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* ahat, int64_t numel,
+                       void* stream) {
+    if (k < 1 || k > CF_GROUP) return CF_E_ARG;
+    if (!idx || !vals || !ahat) return CF_E_NULL;
+    if (int rc = valid_numel(numel)) return rc;
+    if (!aligned16(ahat) || (reinterpret_cast<uintptr_t>(vals) & 1u)) return CF_E_ALIGN;
+    const int64_t slots = numel / CF_GROUP * k;
+    const Range r[3] = {range_of(idx, slots), range_of(vals, slots * 2), range_of(ahat, numel * 4)};
+    const bool out[3] = {false, false, true};
+    if (any_alias(r, out)) return CF_E_ALIAS;
+    if (int rc = check_device()) return rc;
+    return cf::launch_topk_decompress(k, idx, vals, ahat, numel, static_cast<hipStream_t>(stream)) == hipSuccess
                ? CF_OK
                : CF_E_HIP;
 }

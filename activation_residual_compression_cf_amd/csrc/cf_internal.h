@@ -21,6 +21,12 @@ hipError_t launch_compress_ablation(int mode, int bits, int a_dtype, const void*
 hipError_t launch_decompress(int bits, const uint8_t* codes, const float* scales, float* ahat, uint16_t* out,
                              int64_t numel, hipStream_t stream);
 
+// Top-k sparsification of the residual: k of every 128 kept as (index byte, bf16 value).
+hipError_t launch_topk_compress(int k, int a_dtype, const void* a, float* ahat, float* err, uint8_t* idx,
+                                uint16_t* vals, int64_t numel, hipStream_t stream);
+hipError_t launch_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* ahat, int64_t numel,
+                                  hipStream_t stream);
+
 // Low-rank workspace regions (carved from one caller buffer).
 struct LowrankWorkspace {
     float* r;      // batch x m x n residual

@@ -29,27 +29,10 @@
 // multiply rounds once, in the order written; the 2-bit scale uses IEEE division.
 
 #include "cf_internal.h"
+#include "cf_vec.h"
 
 namespace cf {
 namespace {
-
-typedef float vf4 __attribute__((ext_vector_type(4)));
-typedef unsigned vu2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ vf4 ld_nt(const float* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
-}
-__device__ __forceinline__ void st_nt(float* p, vf4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<vf4*>(p));
-}
-
-// 4 consecutive activations at element offset `off`, widened to fp32 (exact).
-__device__ __forceinline__ vf4 load_act4(const uint16_t* __restrict__ a, int64_t off) {
-    const vu2 w = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(a + off));
-    return vf4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-}
-__device__ __forceinline__ vf4 load_act4(const float* __restrict__ a, int64_t off) { return ld_nt(a + off); }
 
 // Value held by lane (this lane ^ mask) / (this lane + delta), as 32-bit words.
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
@@ -181,17 +164,6 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
             if (hl == 0) scales[gi[k]] = s;
         }
     }
-}
-
-// Round-to-nearest-even bf16 of 4 finite floats, packed as 2 words.
-__device__ __forceinline__ vu2 to_bf16x4(vf4 v) {
-    uint32_t q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t u = __float_as_uint(v[i]);
-        q[i] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    }
-    return vu2{q[0] | (q[1] << 16), q[2] | (q[3] << 16)};
 }
 
 template <int BITS, int IPS, int BLOCK, bool OUT16>

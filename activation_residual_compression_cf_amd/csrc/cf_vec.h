@@ -1,0 +1,43 @@
+// Device helpers shared by the element-wise kernels: 4-wide fp32 vectors,
+// non-temporal loads and stores, bf16 widening and rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace cf {
+
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef unsigned vu2 __attribute__((ext_vector_type(2)));
+
+// Non-temporal accesses: every byte of the streamed state is touched once per
+// step, so nothing is worth keeping in L2.
+__device__ __forceinline__ vf4 ld_nt(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, vf4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<vf4*>(p));
+}
+
+// 4 consecutive activations at element offset `off`, widened to fp32 (exact).
+__device__ __forceinline__ vf4 load_act4(const uint16_t* __restrict__ a, int64_t off) {
+    const vu2 w = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(a + off));
+    return vf4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+__device__ __forceinline__ vf4 load_act4(const float* __restrict__ a, int64_t off) { return ld_nt(a + off); }
+
+// Round-to-nearest-even bf16 bits of a finite float, and the exact widening back.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_widen(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round-to-nearest-even bf16 of 4 finite floats, packed as 2 words.
+__device__ __forceinline__ vu2 to_bf16x4(vf4 v) {
+    return vu2{bf16_rne(v.x) | (bf16_rne(v.y) << 16), bf16_rne(v.z) | (bf16_rne(v.w) << 16)};
+}
+
+}  // namespace cf

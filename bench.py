@@ -38,6 +38,12 @@ BYTES_PER_ELEM = {
     "decode1": 4 + 4 + 1 / 8 + 4 / 128,
     "decode2": 4 + 4 + 2 / 8 + 4 / 128,
     "init": 2 + 4 + 4,
+    # top-k sender: the quantizer's 14 B of state traffic, then k index bytes and k bf16
+    # values per group; receiver: the payload and a read + write of the k changed ahat
+    # elements per group
+    "topk12": 2 + 4 + 4 + 4 + 12 * 3 / 128,
+    "topk6": 2 + 4 + 4 + 4 + 6 * 3 / 128,
+    "topk_decode12": 12 * (1 + 2 + 4 + 4) / 128,
 }
 
 
@@ -317,12 +323,16 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, w
         per_layer_row(torch, cf, dev, wl, steps_d, compressed, row)
     if on("lowrank"):
         lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on)
+    if on("topk"):
+        topk_rows(torch, cf, dev, wl, steps_d, compressed, row, on)
     if on("compress2_cogvideo"):
         cogvideo_row(torch, np, cf, gen, dev, per_call, row)
     if on("ef_study"):
         rows["ef_study_flux_1bit"] = ef_study(torch, cf, wl, steps_d)
     if on("lowrank_study"):
         rows["lowrank_study_flux"] = lowrank_study(torch, np, cf, gen, wl, steps_d)
+    if on("sparse_study"):
+        rows["sparse_study_flux"] = sparse_study(torch, cf, wl, steps_d)
     torch.cuda.empty_cache()
     return rows
 
@@ -353,6 +363,32 @@ def quant_rows(torch, cf, dev, wl, steps_d, compressed, per_call, row, on):
     ms = time_calls(torch, lambda: s1.init(steps_d[0], per_call), 8)
     row("init_flux", ms, "init")
     del s1, s2, rx
+
+
+def topk_rows(torch, cf, dev, wl, steps_d, compressed, row, on):
+    """Top-k sparsifier on the whole step in one call: k = 12 (the 2-bit byte budget) and
+    k = 6 (about the 1-bit budget), and the k = 12 receiver decode."""
+    n = wl.slots * wl.numel
+    ahat = torch.empty(n, dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    for k in (12, 6):
+        if not on(f"topk{k}_flux"):
+            continue
+        idx = torch.empty(n // 128 * k, dtype=torch.uint8, device=dev)
+        vals = torch.empty(n // 128 * k, dtype=torch.int16, device=dev)
+        cf.init_state(steps_d[0], ahat, err)
+        it = iter(range(10 ** 9))
+        ms = time_calls(torch, lambda: cf.topk_compress(
+            k, steps_d[compressed[next(it) % len(compressed)]].reshape(-1), ahat, err, idx, vals), 8)
+        row(f"topk{k}_flux", ms, f"topk{k}")
+        if k == 12 and on("topk12_decode_flux"):
+            rx = ahat.clone()
+            ms = time_calls(torch, lambda: cf.topk_decompress(k, idx, vals, rx), 8)
+            row("topk12_decode_flux", ms, "topk_decode12")
+            del rx
+        del idx, vals
+    del ahat, err
+    torch.cuda.empty_cache()
 
 
 def per_layer_row(torch, cf, dev, wl, steps_d, compressed, row):
@@ -437,6 +473,45 @@ def ef_study(torch, cf, wl, steps_d):
     log(f"ef_study: ||A-Ahat||/||dA|| at steps {out['steps']}: EF {out['ef']}, "
         f"no EF {out['no_ef']}, naive {out['naive']}")
     del ef, mirror, naive
+    torch.cuda.empty_cache()
+    return out
+
+
+def sparse_study(torch, cf, wl, steps_d):
+    """Top-k against the quantizers at equal bytes on the FLUX trajectory (all tensors,
+    error feedback on): ||A_t - Ahat_t|| / ||A_t - A_{t-1}|| for 1-bit (20 B per group)
+    beside top-6 (18 B), and 2-bit (36 B) beside top-12 (36 B)."""
+    n = wl.slots * wl.numel
+    dev = steps_d[0].device
+    arms = {"q1": 1, "top6": 6, "q2": 2, "top12": 12}
+    st = {}
+    for name in arms:
+        s = cf.SenderState.create(n, dev)
+        cf.init_state(steps_d[0], s.ahat, s.err)
+        st[name] = s
+    codes = torch.empty(n // 4, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 128, dtype=torch.float32, device=dev)
+    idx = torch.empty(n // 128 * 12, dtype=torch.uint8, device=dev)
+    vals = torch.empty(n // 128 * 12, dtype=torch.int16, device=dev)
+    out = {"steps": [], **{k: [] for k in arms}}
+    for t in range(1, len(steps_d)):
+        a = steps_d[t].reshape(-1)
+        for name, p in arms.items():
+            s = st[name]
+            if name.startswith("q"):
+                cf.compress(p, a, s.ahat, s.err, codes[: n * p // 8], scales)
+            else:
+                cf.topk_compress(p, a, s.ahat, s.err, idx[: n // 128 * p], vals[: n // 128 * p])
+        if t in (1, 2, 4, 8, 16, len(steps_d) - 1):
+            a32 = a.float()
+            step = torch.linalg.norm(a32 - steps_d[t - 1].reshape(-1).float()).item()
+            out["steps"].append(t)
+            for name in arms:
+                out[name].append(round(torch.linalg.norm(a32 - st[name].ahat).item() / step, 4))
+            del a32
+    log("sparse_study: ||A-Ahat||/||dA|| at steps " + str(out["steps"]) + ": " +
+        ", ".join(f"{k} {out[k]}" for k in arms))
+    del st, codes, scales, idx, vals
     torch.cuda.empty_cache()
     return out
 

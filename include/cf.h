@@ -29,8 +29,8 @@
  *     one call (one "slab"), since no group straddles two tensors when every
  *     tensor's size is a multiple of 128.
  *   - Every pointer must be 16-byte aligned, except `scales` (one float per
- *     group), which needs 4-byte alignment; input and output ranges must not
- *     overlap.
+ *     group), which needs 4-byte alignment, and the top-k payload (see there);
+ *     input and output ranges must not overlap.
  *   - Results are deterministic: no atomics, fixed reduction orders.
  *   - Calls on different streams with disjoint buffers may run concurrently.
  *   - Non-finite inputs give unspecified (but memory-safe) results.
@@ -51,7 +51,7 @@ enum {
     CF_E_NULL = -1,      /* a required pointer is NULL */
     CF_E_SHAPE = -2,     /* numel / m / n / rank / batch out of range */
     CF_E_ALIGN = -3,     /* a pointer is misaligned (16 bytes; scales 4 bytes) */
-    CF_E_ARG = -4,       /* bits, dtype, factor_bits or iters not supported */
+    CF_E_ARG = -4,       /* bits, k, dtype, factor_bits or iters not supported */
     CF_E_ALIAS = -5,     /* an output range overlaps another operand */
     CF_E_WORKSPACE = -6, /* workspace missing or too small */
     CF_E_DEVICE = -7,    /* current device is not gfx950 */
@@ -130,6 +130,37 @@ int cf_decompress_bf16(int bits, const uint8_t* codes, const float* scales, floa
  */
 int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const void* a_prev, float* ahat,
                          uint8_t* codes, float* scales, int64_t numel, void* stream);
+
+/*
+ * Sender step, top-k sparsification of the residual (Limitations: sparsity is
+ * the other fast compressor family beside quantization; the pages give no rule,
+ * and the one built here is the following).  Per group g of 128 contiguous
+ * elements:
+ *   r = a - ahat                                               (fp32)
+ *   keep the k elements of largest |r|, ordered by the bit pattern of |r| (the
+ *   magnitude order for non-NaN values), equal magnitudes going to the lower
+ *   index;  for each kept element i, in increasing i:
+ *     idx[g*k + slot] = i (0..127);  vals[g*k + slot] = v = RNE bf16 of r[i];
+ *     ahat[i] = ahat[i] + widen(v)
+ *   err = a - ahat for all 128 elements (the dropped residuals stay in err).
+ *   1 <= k <= 128 (k = 12 spends the 2-bit budget of 36 bytes per group).
+ *   idx: numel/128*k bytes, any alignment; vals: numel/128*k bf16 (raw 16-bit),
+ *   2-byte aligned; a, ahat, err: 16-byte aligned.
+ *   a: in; ahat: in/out; err, idx, vals: out.
+ */
+int cf_topk_compress(int k, int a_dtype, const void* a, float* ahat, float* err, uint8_t* idx, uint16_t* vals,
+                     int64_t numel, void* stream);
+
+/*
+ * Receiver step, top-k: ahat[g*128 + (idx[g*k+s] & 127)] += widen(vals[g*k+s]) for
+ * every slot s, the sender's own update, so the reconstructions agree bit for bit.
+ * Only the low 7 bits of an index byte are used, so any payload stays inside its
+ * group; a payload that repeats an index within a group (the sender never does)
+ * gives an unspecified value at that element.
+ *   idx, vals: in (as produced by cf_topk_compress); ahat: in/out, 16-byte aligned.
+ */
+int cf_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* ahat, int64_t numel,
+                       void* stream);
 
 /*
  * Sender step, Compact-Lowrank (Approach: low-rank compression of the residual

@@ -184,3 +184,39 @@ def test_ablation_and_bf16_decode_validation(L):
     assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), P(0x40008), 128, None) == CF_E_ALIGN
     assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), P(0x30000), 128, None) == CF_E_ALIAS
     assert L.cf_decompress_bf16(1, P(0x10000), P(0x20000), P(0x30000), P(0x40000), 128, None) == CF_E_DEVICE
+
+
+def test_topk_validation(L):
+    L.cf_topk_compress.argtypes = ([ctypes.c_int] * 2 + [ctypes.c_void_p] * 5 +
+                                   [ctypes.c_int64, ctypes.c_void_p])
+    L.cf_topk_decompress.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 3 +
+                                     [ctypes.c_int64, ctypes.c_void_p])
+
+    def call(k=12, dt=0, a=0x100000, ah=0x200000, e=0x300000, i=0x400000, v=0x500000, n=1280):
+        return L.cf_topk_compress(k, dt, P(a) if a else None, P(ah) if ah else None,
+                                  P(e) if e else None, P(i) if i else None, P(v) if v else None,
+                                  n, None)
+
+    assert call(k=0) == CF_E_ARG
+    assert call(k=129) == CF_E_ARG
+    assert call(dt=2) == CF_E_ARG
+    assert call(i=0) == CF_E_NULL
+    assert call(v=0) == CF_E_NULL
+    assert call(n=1000) == CF_E_SHAPE
+    assert call(e=0x300008) == CF_E_ALIGN
+    assert call(v=0x500001) == CF_E_ALIGN
+    assert call(i=0x400001, v=0x500002) == CF_E_DEVICE     # idx bytes need no alignment
+    assert call(i=0x500000 - 10 * 12 + 1) == CF_E_ALIAS       # idx runs into vals
+    assert call(i=0x500000 - 10 * 12) == CF_E_DEVICE          # adjacent is fine
+    assert call(v=0x300000 + 1280 * 4 - 2) == CF_E_ALIAS      # vals overlaps err's tail
+    assert call(k=128) == CF_E_DEVICE
+    assert call() == CF_E_DEVICE
+    dec = lambda k=12, i=0x400000, v=0x500000, ah=0x200000, n=1280: L.cf_topk_decompress(
+        k, P(i) if i else None, P(v) if v else None, P(ah) if ah else None, n, None)
+    assert dec(k=0) == CF_E_ARG
+    assert dec(v=0) == CF_E_NULL
+    assert dec(n=0) == CF_E_SHAPE
+    assert dec(ah=0x200004) == CF_E_ALIGN
+    assert dec(v=0x500001) == CF_E_ALIGN
+    assert dec(i=0x200000 + 1280 * 4 - 1) == CF_E_ALIAS       # idx overlapping the output mirror
+    assert dec() == CF_E_DEVICE
