@@ -10,17 +10,27 @@
 // increasing index order as one index byte and the round-to-nearest-even bf16 of
 // r each; ahat adds the sent values, err = a - ahat.
 //
-// Work mapping: the same as the quantizers.  A half wave (32 lanes) owns one
-// group, lane j holds the 4 consecutive elements 4j .. 4j+3, and each load or
-// store instruction covers one contiguous span.  Selection needs no sort and no
-// LDS.  The keys are the bit patterns of |r| (their integer order is the
-// magnitude order), and the k-th largest key T is found bit by bit from the top:
-// a candidate T | 2^b is kept while at least k keys reach it, and the counts come
-// from wave ballots, popcounted per half.  The search stops early once exactly k
-// keys reach T, which smooth data does after about 15 of the 31 bits.  Keys above
-// T are kept, and so are the first k - #(key > T) keys equal to T in index order
-// (a ballot prefix count).  The same prefix count over the kept flags gives each
-// kept element its output slot.
+// Work mapping.  One wave owns one group: lane l holds elements 2l and 2l+1, so the
+// threshold search is wave-uniform and every count is a 64-bit ballot popcount on the
+// scalar unit.  Selection needs no sort.  The keys are the bit patterns of |r|, whose
+// integer order is the magnitude order, and the k-th largest key T is found bit by bit
+// from the top: a candidate T | 2^b is kept while at least k keys reach it.  The
+// candidate and the select run on the vector unit (T sits in a VGPR) and the counts on
+// the scalar unit, so the two halves of a step issue side by side.  The 31 steps are
+// unrolled and stop as soon as exactly k keys reach the candidate.  Keys above T are
+// kept, and so are the first k - #(key > T) keys equal to T in index order (a ballot
+// prefix count); the same prefix count over the kept flags gives each kept element its
+// output slot.
+//
+// A wave takes kPerWave consecutive groups in straight-line code, with each group's loads
+// issued two groups ahead.  No memory operation sits under a data-dependent branch, so
+// the compiler can wait for exactly the loads a group needs.  The payload of the wave's
+// groups is one contiguous span of the output (kPerWave*k index bytes, as many bf16
+// values).  It is staged in LDS and written as whole dwords once the wave is done; the
+// per-element byte stores it replaces cost about a tenth of the kernel's time.  When the
+// payload pointers are not 4-byte aligned, and for the last wave's ragged tail, kept
+// elements store directly through buffer stores whose unselected lanes get an
+// out-of-range offset, which the hardware drops.
 
 #include "cf_internal.h"
 #include "cf_vec.h"
@@ -28,137 +38,217 @@
 namespace cf {
 namespace {
 
-constexpr uint64_t kLoHalf = 0x00000000ffffffffull;
+typedef float vf2 __attribute__((ext_vector_type(2)));
 
-// Number of lanes in this lane's half wave whose predicate holds.  The two
-// popcounts are wave-uniform; only the final select depends on the lane.
-__device__ __forceinline__ int half_count(bool pred, bool upper) {
-    const uint64_t m = __ballot(pred);
-    const int lo = __popc(static_cast<uint32_t>(m));
-    const int hi = __popc(static_cast<uint32_t>(m >> 32));
-    return upper ? hi : lo;
+// Groups per wave and how far ahead their loads are issued.
+constexpr int kPerWave = 4;
+constexpr int kLead = 2;
+constexpr int kBlock = 512;
+constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past any range: the store is dropped
+
+// Two consecutive activations of a lane, as loaded, and widened to fp32.
+__device__ __forceinline__ uint32_t load_pair(const uint16_t* a, int64_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a + off));
 }
+__device__ __forceinline__ vf2 load_pair(const float* a, int64_t off) {
+    return __builtin_nontemporal_load(reinterpret_cast<const vf2*>(a + off));
+}
+__device__ __forceinline__ vf2 widen_pair(uint32_t w) {
+    return vf2{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+}
+__device__ __forceinline__ vf2 widen_pair(vf2 w) { return w; }
 
-template <typename ActT, int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_topk_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
-                                                         float* __restrict__ err, uint8_t* __restrict__ idx,
-                                                         uint16_t* __restrict__ vals, int k, int64_t ngroups) {
-    constexpr int kWaves = BLOCK / 64;
-    const int lane = threadIdx.x & 63;
-    const int hl = lane & 31;
-    const bool upper = lane >= 32;
-    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (tile * 2 >= ngroups) return;  // uniform per wave
-    const int64_t g = tile * 2 + (upper ? 1 : 0);
-    const bool ok = g < ngroups;
-    const int64_t gi = ok ? g : ngroups - 1;  // ragged tail: recompute the last group, skip the stores
-    const int64_t off = gi * kGroup + hl * 4;
-
-    const vf4 x = load_act4(a, off);
-    const vf4 h = ld_nt(ahat + off);
-    const vf4 r = x - h;
-    uint32_t key[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) key[j] = __float_as_uint(r[j]) & 0x7fffffffu;
-
-    // T: the k-th largest key of the group (or a prefix of it that exactly k keys reach).
-    uint32_t T = 0;
-    int cntT = kGroup;
-    for (int b = 30; b >= 0; --b) {
-        if (__all(cntT == k)) break;
-        const uint32_t cand = T | (1u << b);
-        const int cnt = half_count(key[0] >= cand, upper) + half_count(key[1] >= cand, upper) +
-                        half_count(key[2] >= cand, upper) + half_count(key[3] >= cand, upper);
-        if (cnt >= k) {
-            T = cand;
-            cntT = cnt;
+// Where a group's payload goes: LDS staging slots, or the output through buffer stores.
+struct StagedPayload {
+    uint8_t* idx;  // LDS, this group's k slots
+    uint16_t* val;
+    __device__ void put(int slot, bool keep, uint32_t i, uint32_t v) const {
+        if (keep) {
+            idx[slot] = static_cast<uint8_t>(i);
+            val[slot] = static_cast<uint16_t>(v);
         }
     }
-
-    // Keys above T are kept; of the keys equal to T, the lowest-indexed k - #above.
-    const uint64_t below = ((1ull << lane) - 1ull) & (upper ? ~kLoHalf : kLoHalf);
-    int above = 0, eq_before = 0;
-    bool eq[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        above += half_count(key[j] > T, upper);
-        eq[j] = key[j] == T;
-        eq_before += __popcll(__ballot(eq[j]) & below);
+};
+struct DirectPayload {
+    __amdgpu_buffer_rsrc_t idx, val;  // this group's k bytes / k values
+    __device__ void put(int slot, bool keep, uint32_t i, uint32_t v) const {
+        const uint32_t o = keep ? static_cast<uint32_t>(slot) : kDrop;
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(i), idx, o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v), val, keep ? o * 2 : kDrop, 0, 0);
     }
+};
+
+__device__ __forceinline__ DirectPayload direct_payload(uint8_t* idx, uint16_t* vals, int64_t g, int k) {
+    return {__builtin_amdgcn_make_buffer_rsrc(idx + g * k, static_cast<short>(0), k, 0x00020000),
+            __builtin_amdgcn_make_buffer_rsrc(vals + g * k, static_cast<short>(0), 2 * k, 0x00020000)};
+}
+
+// One group on one wave: selection, state update, payload.
+template <typename RawT, typename Payload>
+__device__ __forceinline__ void topk_group(RawT raw, vf2 h, int64_t g, int lane, int k, float* __restrict__ ahat,
+                                           float* __restrict__ err, const Payload& pay) {
+    const vf2 x = widen_pair(raw);
+    const float r0 = x.x - h.x, r1 = x.y - h.y;
+    const uint32_t key0 = __float_as_uint(r0) & 0x7fffffffu, key1 = __float_as_uint(r1) & 0x7fffffffu;
+    // T is wave-uniform but kept in a VGPR (a plain register move the compiler cannot
+    // fold), so candidate and select stay on the vector unit.
+    uint32_t T;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(T));
+    if (k < kGroup) {
+#pragma unroll
+        for (int b = 30; b >= 0; --b) {
+            const uint32_t cand = T | (1u << b);
+            const int cnt = __popcll(__ballot(key0 >= cand)) + __popcll(__ballot(key1 >= cand));
+            if (cnt >= k) T = cand;
+            if (cnt == k) break;  // exactly the keys >= T are kept
+        }
+    }
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int above = __popcll(__ballot(key0 > T)) + __popcll(__ballot(key1 > T));
     const int need = k - above;
-    bool sel[4];
-    int sel_before = 0;
+    const bool eq0 = key0 == T, eq1 = key1 == T;
+    const int eq_before = __popcll(__ballot(eq0) & below) + __popcll(__ballot(eq1) & below);
+    const bool sel0 = key0 > T || (eq0 && eq_before < need);
+    const bool sel1 = key1 > T || (eq1 && eq_before + (eq0 ? 1 : 0) < need);
+    const int slot0 = __popcll(__ballot(sel0) & below) + __popcll(__ballot(sel1) & below);
+    const int slot1 = slot0 + (sel0 ? 1 : 0);
+    const uint32_t v0 = bf16_rne(r0), v1 = bf16_rne(r1);
+    const float hn0 = sel0 ? h.x + bf16_widen(v0) : h.x;
+    const float hn1 = sel1 ? h.y + bf16_widen(v1) : h.y;
+    const int64_t off = g * kGroup + lane * 2;
+    __builtin_nontemporal_store(vf2{hn0, hn1}, reinterpret_cast<vf2*>(ahat + off));
+    __builtin_nontemporal_store(vf2{x.x - hn0, x.y - hn1}, reinterpret_cast<vf2*>(err + off));
+    pay.put(slot0, sel0, lane * 2, v0);
+    pay.put(slot1, sel1, lane * 2 + 1, v1);
+}
+
+template <typename ActT, bool STAGED>
+__global__ __launch_bounds__(kBlock) void k_topk_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
+                                                          float* __restrict__ err, uint8_t* __restrict__ idx,
+                                                          uint16_t* __restrict__ vals, int k, int64_t ngroups) {
+    using RawT = decltype(load_pair(a, 0));
+    constexpr int kWaves = kBlock / 64;
+    __shared__ uint32_t sidx[STAGED ? kWaves : 1][kPerWave * kGroup / 4];
+    __shared__ uint32_t sval[STAGED ? kWaves : 1][kPerWave * kGroup / 2];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kPerWave;
+    if (g0 >= ngroups) return;
+    if (g0 + kPerWave > ngroups) {  // ragged tail of the last wave
+        for (int64_t g = g0; g < ngroups; ++g) {
+            const int64_t off = g * kGroup + lane * 2;
+            topk_group(load_pair(a, off), __builtin_nontemporal_load(reinterpret_cast<const vf2*>(ahat + off)), g,
+                       lane, k, ahat, err, direct_payload(idx, vals, g, k));
+        }
+        return;
+    }
+    RawT xr[kPerWave];
+    vf2 hr[kPerWave];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        sel[j] = key[j] > T || (eq[j] && eq_before < need);
-        eq_before += eq[j] ? 1 : 0;
+    for (int j = 0; j < kLead; ++j) {
+        const int64_t off = (g0 + j) * kGroup + lane * 2;
+        xr[j] = load_pair(a, off);
+        hr[j] = __builtin_nontemporal_load(reinterpret_cast<const vf2*>(ahat + off));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sel_before += __popcll(__ballot(sel[j]) & below);
-
-    vf4 hn = h;
-    uint32_t v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        v[j] = bf16_rne(r[j]);
-        if (sel[j]) hn[j] = h[j] + bf16_widen(v[j]);
-    }
-    const vf4 e = x - hn;
-
-    if (ok) {
-        st_nt(ahat + off, hn);
-        st_nt(err + off, e);
-        uint8_t* gidx = idx + gi * k;
-        uint16_t* gval = vals + gi * k;
-        int slot = sel_before;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (sel[j]) {
-                gidx[slot] = static_cast<uint8_t>(hl * 4 + j);
-                gval[slot] = static_cast<uint16_t>(v[j]);
-                ++slot;
-            }
+    for (int j = 0; j < kPerWave; ++j) {
+        if (j + kLead < kPerWave) {
+            const int64_t off = (g0 + j + kLead) * kGroup + lane * 2;
+            xr[j + kLead] = load_pair(a, off);
+            hr[j + kLead] = __builtin_nontemporal_load(reinterpret_cast<const vf2*>(ahat + off));
+        }
+        if constexpr (STAGED) {
+            const StagedPayload pay{reinterpret_cast<uint8_t*>(sidx[wave]) + j * k,
+                                    reinterpret_cast<uint16_t*>(sval[wave]) + j * k};
+            topk_group(xr[j], hr[j], g0 + j, lane, k, ahat, err, pay);
+        } else {
+            topk_group(xr[j], hr[j], g0 + j, lane, k, ahat, err, direct_payload(idx, vals, g0 + j, k));
         }
     }
-}
-
-// Receiver: ahat[g*128 + idx] += widened value, one half wave per group, lane j
-// taking entries j, j + 32, ...  Index bytes are masked to 7 bits so any payload
-// stays inside its group.
-template <int BLOCK>
-__global__ __launch_bounds__(BLOCK) void k_topk_decompress(const uint8_t* __restrict__ idx,
-                                                           const uint16_t* __restrict__ vals,
-                                                           float* __restrict__ ahat, int k, int64_t ngroups) {
-    constexpr int kWaves = BLOCK / 64;
-    const int lane = threadIdx.x & 63;
-    const int hl = lane & 31;
-    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    const int64_t g = tile * 2 + (lane >> 5);
-    if (g >= ngroups) return;
-    for (int j = hl; j < k; j += 32) {
-        const int64_t t = g * k + j;
-        float* p = ahat + g * kGroup + (idx[t] & 127);
-        *p = *p + bf16_widen(vals[t]);
+    if constexpr (STAGED) {
+        // LDS traffic of one wave is processed in order; the fences keep the compiler from
+        // moving the reads of other lanes' slots above the writes.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // kPerWave*k index bytes at idx + g0*k and as many values at vals + g0*k, both
+        // dword aligned (g0 is a multiple of 4 and the launcher checked the pointers)
+        uint32_t* gi = reinterpret_cast<uint32_t*>(idx + g0 * k);
+        uint32_t* gv = reinterpret_cast<uint32_t*>(vals + g0 * k);
+        const int nwi = kPerWave * k / 4, nwv = kPerWave * k / 2;
+        for (int i = lane; i < nwi; i += 64) gi[i] = sidx[wave][i];
+        for (int i = lane; i < nwv; i += 64) gv[i] = sval[wave][i];
     }
 }
 
-template <typename K>
-hipError_t launch_pairs(K kernel, int64_t ngroups, int block, void** args, hipStream_t stream) {
-    const int64_t tiles = (ngroups + 1) / 2;
-    const int64_t blocks = (tiles + block / 64 - 1) / (block / 64);
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
-                           dim3(block), args, 0, stream);
+// Receiver: ahat[g*128 + (idx & 127)] += widened value, as one dense pass.  A wave
+// owns a group (lane l: elements 2l, 2l+1) and takes kPerWave of them; it reads the
+// reconstruction once and writes it once, with non-temporal accesses.  The payload
+// of a group (at most 128 slots) is read by lanes slot and slot + 64 through buffer
+// loads (slots >= k are out of range and read as 0 without touching memory) and
+// scattered into a per-wave LDS table of 128 words, tagged with the group's position
+// in the wave so that the table never needs clearing; each lane then reads its two
+// elements' words and adds the value where the tag matches.  Scattered 4-byte updates
+// would touch most 64-byte sectors of a group anyway and leave them partly written.
+__global__ __launch_bounds__(kBlock) void k_topk_decompress(const uint8_t* __restrict__ idx,
+                                                            const uint16_t* __restrict__ vals,
+                                                            float* __restrict__ ahat, int k, int64_t ngroups) {
+    constexpr int kWaves = kBlock / 64;
+    __shared__ uint32_t table[kWaves][kGroup];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int64_t g0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kPerWave;
+    if (g0 >= ngroups) return;
+    table[wave][lane] = 0;
+    table[wave][lane + 64] = 0;
+    vf2 h[kPerWave];
+    uint32_t slot_idx[kPerWave][2], slot_val[kPerWave][2];
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+        const int64_t g = g0 + j < ngroups ? g0 + j : ngroups - 1;  // the tail re-reads the last group
+        h[j] = __builtin_nontemporal_load(reinterpret_cast<const vf2*>(ahat + g * kGroup + lane * 2));
+        const auto ri = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(idx + g * k), static_cast<short>(0),
+                                                          k, 0x00020000);
+        const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vals + g * k),
+                                                          static_cast<short>(0), 2 * k, 0x00020000);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            slot_idx[j][s] = __builtin_amdgcn_raw_buffer_load_b8(ri, lane + 64 * s, 0, 0);
+            slot_val[j][s] = __builtin_amdgcn_raw_buffer_load_b16(rv, (lane + 64 * s) * 2, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+        const uint32_t tag = static_cast<uint32_t>(j + 1) << 16;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            if (lane + 64 * s < k) table[wave][slot_idx[j][s] & 127] = tag | slot_val[j][s];
+        // one wave's LDS traffic is processed in order; the fences only keep the compiler
+        // from moving these reads above the other lanes' writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t w0 = table[wave][lane * 2], w1 = table[wave][lane * 2 + 1];
+        const float hn0 = (w0 & 0xffff0000u) == tag ? h[j].x + bf16_widen(w0 & 0xffffu) : h[j].x;
+        const float hn1 = (w1 & 0xffff0000u) == tag ? h[j].y + bf16_widen(w1 & 0xffffu) : h[j].y;
+        if (g0 + j < ngroups)
+            __builtin_nontemporal_store(vf2{hn0, hn1}, reinterpret_cast<vf2*>(ahat + (g0 + j) * kGroup + lane * 2));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 }
-
-// Calls of at least this many groups take 256-thread blocks, smaller ones 128.
-constexpr int64_t kLargeTopk = int64_t(1) << 17;
 
 template <typename ActT>
 hipError_t run_topk(const ActT* a, float* ahat, float* err, uint8_t* idx, uint16_t* vals, int k, int64_t ngroups,
                     hipStream_t stream) {
     void* args[] = {&a, &ahat, &err, &idx, &vals, &k, &ngroups};
-    if (ngroups >= kLargeTopk) return launch_pairs(&k_topk_compress<ActT, 256>, ngroups, 256, args, stream);
-    return launch_pairs(&k_topk_compress<ActT, 128>, ngroups, 128, args, stream);
+    const int64_t waves = (ngroups + kPerWave - 1) / kPerWave;
+    const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
+    const bool staged = ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(vals)) & 3u) == 0;
+    const void* fn = staged ? reinterpret_cast<const void*>(&k_topk_compress<ActT, true>)
+                            : reinterpret_cast<const void*>(&k_topk_compress<ActT, false>);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args, 0, stream);
 }
 
 }  // namespace
@@ -174,7 +264,10 @@ hipError_t launch_topk_decompress(int k, const uint8_t* idx, const uint16_t* val
                                   hipStream_t stream) {
     int64_t ng = numel / kGroup;
     void* args[] = {&idx, &vals, &ahat, &k, &ng};
-    return launch_pairs(&k_topk_decompress<256>, ng, 256, args, stream);
+    const int64_t waves = (ng + kPerWave - 1) / kPerWave;
+    const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_topk_decompress), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kBlock), args, 0, stream);
 }
 
 }  // namespace cf

@@ -39,11 +39,11 @@ BYTES_PER_ELEM = {
     "decode2": 4 + 4 + 2 / 8 + 4 / 128,
     "init": 2 + 4 + 4,
     # top-k sender: the quantizer's 14 B of state traffic, then k index bytes and k bf16
-    # values per group; receiver: the payload and a read + write of the k changed ahat
-    # elements per group
+    # values per group; receiver: the payload and one read + write of the mirror (k
+    # scattered 4-byte updates per group touch most 64-byte sectors anyway)
     "topk12": 2 + 4 + 4 + 4 + 12 * 3 / 128,
     "topk6": 2 + 4 + 4 + 4 + 6 * 3 / 128,
-    "topk_decode12": 12 * (1 + 2 + 4 + 4) / 128,
+    "topk_decode12": 4 + 4 + 12 * 3 / 128,
 }
 
 

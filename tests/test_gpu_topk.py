@@ -128,6 +128,31 @@ def test_ties_and_special_values(cf, dev, O, k):
     assert np.array_equal(host(er), er_o)
 
 
+@pytest.mark.parametrize("k", [12, 5])
+def test_unaligned_payload_pointers(cf, dev, O, k):
+    """Index and value buffers that are not 4-byte aligned (1 and 2 bytes off) take the
+    direct-store path; 203 groups leave a ragged tail."""
+    say(f"top-k unaligned payload k={k}")
+    wl = gen.Workload("unal", 203, 128, 1, 2, "bf16", True)
+    tr = gen.Trajectory(wl, 9)
+    A0, A1 = tr.next()[0], tr.next()[0]
+    G = 203
+    ah_o, er_o = gen.as_f32(A0).reshape(-1).copy(), np.zeros(G * 128, np.float32)
+    i_o, v_o = O.topk_compress(k, A1.reshape(-1).copy(), ah_o, er_o)
+    ah = to_dev(gen.as_f32(A0).reshape(-1).copy(), dev)
+    er = torch.zeros_like(ah)
+    ibuf = torch.zeros(G * k + 16, dtype=torch.uint8, device=dev)
+    vbuf = torch.zeros(G * k + 16, dtype=torch.int16, device=dev)
+    idx, vals = ibuf[1:1 + G * k], vbuf[1:1 + G * k]
+    cf.topk_compress(k, to_dev(A1.reshape(-1), dev), ah, er, idx, vals)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), i_o), mismatch(host(idx), i_o)
+    assert np.array_equal(_u16(vals), v_o), mismatch(_u16(vals), v_o)
+    assert np.array_equal(host(ah), ah_o) and np.array_equal(host(er), er_o)
+    assert not host(ibuf[0:1]).any() and not host(ibuf[1 + G * k:]).any()  # guard bytes
+    assert not host(vbuf[0:1]).any() and not host(vbuf[1 + G * k:]).any()
+
+
 def test_flux_full_shape_one_call(cf, dev, O):
     """114 tensors of 1024 x 3072 bf16 (a FLUX.1-dev shard's layer activations) in one call,
     k = 12 (the 2-bit byte budget)."""
