@@ -400,7 +400,20 @@ def per_layer_row(torch, cf, dev, wl, steps_d, compressed, row):
     ms = time_calls(torch, lambda: s1.compress(steps_d[compressed[next(it2) % len(compressed)]],
                                                2), 8)
     row("compress1_flux_per_layer", ms, "compress1")
-    del s1
+    # the same 57 calls captured once per input step in a HIP graph and replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for j in range(4):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            s1.compress(steps_d[compressed[j % len(compressed)]], 2)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    it3 = iter(range(10 ** 9))
+    ms = time_calls(torch, lambda: graphs[next(it3) % len(graphs)].replay(), 8)
+    row("compress1_flux_per_layer_graph", ms, "compress1")
+    del graphs, s1
     torch.cuda.empty_cache()
 
 

@@ -1,0 +1,94 @@
+"""The C ABI under HIP graph capture: a per-layer loop of compress and decode calls (one
+call per layer's K and V, the serving pattern) is captured once on a side stream and
+replayed on successive steps. Every replay must reproduce an eager run bit for bit.
+Between replays the test does eager work of its own and synchronises, so a graph that
+only works when replayed back to back would fail."""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import gen
+from gpu_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cf():
+    from activation_residual_compression_cf_amd import cf as _cf
+
+    return _cf
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_per_layer_loop_graph_matches_eager(cf, bits):
+    dev = cf.require_device()
+    wl = gen.Workload("graph", 256, 3072, 6, 5, "bf16", True)  # 3 layers x (K, V)
+    tr = gen.Trajectory(wl, 11)
+    A = [to_dev(tr.next(), dev) for _ in range(wl.steps)]
+    say(f"graph capture of the per-layer loop, bits={bits}")
+    eager_tx = cf.Slab(wl.slots, wl.numel, bits, dev)
+    eager_rx = cf.Slab(wl.slots, wl.numel, bits, dev, receiver=True)
+    graph_tx = cf.Slab(wl.slots, wl.numel, bits, dev)
+    graph_rx = cf.Slab(wl.slots, wl.numel, bits, dev, receiver=True)
+    for s in (eager_tx, eager_rx, graph_tx, graph_rx):
+        s.init(A[0], per_call=2)
+    static_a = torch.empty_like(A[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        graph_tx.compress(static_a, per_call=2)
+        graph_rx.decompress(graph_tx.codes, graph_tx.scales, per_call=2)
+    torch.cuda.synchronize()
+    for t in range(1, wl.steps):
+        static_a.copy_(A[t])
+        g.replay()
+        eager_tx.compress(A[t], per_call=2)
+        eager_rx.decompress(eager_tx.codes, eager_tx.scales, per_call=2)
+        junk = (A[t].float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for x, y in ((graph_tx.ahat, eager_tx.ahat), (graph_tx.err, eager_tx.err),
+                     (graph_tx.codes, eager_tx.codes), (graph_tx.scales, eager_tx.scales),
+                     (graph_rx.ahat, eager_rx.ahat)):
+            assert torch.equal(x, y), f"replay {t} differs from the eager run"
+        assert torch.equal(graph_rx.ahat, graph_tx.ahat)
+
+
+def test_topk_graph_matches_eager(cf):
+    dev = cf.require_device()
+    wl = gen.Workload("graphk", 256, 3072, 4, 4, "bf16", True)
+    tr = gen.Trajectory(wl, 12)
+    A = [to_dev(tr.next().reshape(-1), dev) for _ in range(wl.steps)]
+    say("graph capture of top-k compress + decode")
+    n, k = A[0].numel(), 12
+    st = {}
+    for name in ("eager", "graph"):
+        ah = torch.empty(n, dtype=torch.float32, device=dev)
+        er = torch.empty_like(ah)
+        rx = torch.empty_like(ah)
+        cf.init_state(A[0], ah, er)
+        cf.init_state(A[0], rx)
+        idx = torch.empty(n // 128 * k, dtype=torch.uint8, device=dev)
+        vals = torch.empty(n // 128 * k, dtype=torch.int16, device=dev)
+        st[name] = (ah, er, rx, idx, vals)
+    static_a = torch.empty_like(A[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    ah, er, rx, idx, vals = st["graph"]
+    with torch.cuda.graph(g, stream=side):
+        cf.topk_compress(k, static_a, ah, er, idx, vals)
+        cf.topk_decompress(k, idx, vals, rx)
+    torch.cuda.synchronize()
+    for t in range(1, wl.steps):
+        static_a.copy_(A[t])
+        g.replay()
+        e = st["eager"]
+        cf.topk_compress(k, A[t], e[0], e[1], e[3], e[4])
+        cf.topk_decompress(k, e[3], e[4], e[2])
+        torch.cuda.synchronize()
+        for x, y in zip(st["graph"], st["eager"]):
+            assert torch.equal(x, y), f"replay {t} differs from the eager run"
