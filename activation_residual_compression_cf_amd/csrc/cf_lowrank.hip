@@ -47,7 +47,7 @@ typedef unsigned vu2 __attribute__((ext_vector_type(2)));
 constexpr int kSegCols = 512;   // columns per projection segment
 constexpr int kProjRows = 256;  // rows per projection workgroup (4 waves x 64)
 constexpr int kBackCols = 256;  // columns per back-projection workgroup
-constexpr int kRecRows = 128;   // reconstruction workgroup: 128 rows x 256 columns
+constexpr int kRecRows = 32;    // reconstruction workgroup: 32 rows x 256 columns
 constexpr int kRecCols = 256;
 
 __device__ __forceinline__ vf4 mfma4(float a, float b, vf4 c) {
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const d
 // accumulates Q^T[kk][col] = sum_rows P[row][kk] r[row][col] with MFMA (4 rows per
 // k-slice; a lane's float4 of r gives 4 column sets).  No cross-wave reduction.
 template <int KT>
-__global__ __launch_bounds__(256) void k_lr_backproject(const float* __restrict__ r, const float* __restrict__ p,
+__global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const float* p,
                                                          float* __restrict__ qt, int64_t m, int64_t n,
                                                          int64_t batch, int64_t total) {
     constexpr int kp = 16 * KT;
@@ -401,31 +401,36 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* __restrict_
 #pragma unroll
         for (int t = 0; t < KT; ++t) acc[i][t] = vf4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t col = c0 + 4 * lane;  // staging column of this lane
-    constexpr int PPT = (kStage * kp + 255) / 256;  // P values staged per thread
-    vf4 rq[4];
-    float pq[PPT];
-    auto fetch = [&](int64_t sr) {
+    // Staging column of this lane, clamped into the tensor: a column past n loads a
+    // valid column whose products only reach output columns that are never stored.
+    const int64_t col = c0 + 4 * lane < n ? c0 + 4 * lane : n - 4;
+    const int64_t nst = m / kStage;
+    // Three stage buffers rotated by name (the loop is unrolled by three), two stages
+    // in flight while one is multiplied.  Every load is unconditional (stages past the
+    // end reload the last one and are never used), so the compiler waits for exactly
+    // the buffer a stage needs.
+    vf4 rq[3][4];
+    float pq[3][KT];
+    auto fetch = [&](vf4 (&rx)[4], float (&px)[KT], int64_t st) {
+        const int64_t sr = (st < nst ? st : nst - 1) * kStage;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            rq[q] = col < n ? ld4(rb + (sr + 4 * wave + q) * n + col) : vf4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) rx[q] = ld4(rb + (sr + 4 * wave + q) * n + col);
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
+        for (int j = 0; j < KT; ++j) {  // kStage * kp = 256 KT values, KT per thread
             const int e = threadIdx.x + 256 * j;
-            pq[j] = e < kStage * kp ? pb[(sr + e / kp) * kp + e % kp] : 0.0f;
+            px[j] = pb[(sr + e / kp) * kp + e % kp];
         }
     };
-    fetch(0);
-    for (int64_t sr = 0; sr < m; sr += kStage) {
+    auto stage = [&](vf4 (&rx)[4], float (&px)[KT], int64_t st) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&slab[4 * wave + q][4 * lane]) = rq[q];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&slab[4 * wave + q][4 * lane]) = rx[q];
 #pragma unroll
-        for (int j = 0; j < PPT; ++j) {
+        for (int j = 0; j < KT; ++j) {
             const int e = threadIdx.x + 256 * j;
-            if (e < kStage * kp) ps[e / kp][e % kp] = pq[j];
+            ps[e / kp][e % kp] = px[j];
         }
         __syncthreads();
-        if (sr + kStage < m) fetch(sr + kStage);  // next stage's loads overlap the MFMAs
+        fetch(rx, px, st + 3);  // refill this buffer three stages ahead
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const vf4 rv = *reinterpret_cast<const vf4*>(&slab[4 * rg + lg][64 * wave + 4 * li]);
@@ -438,6 +443,16 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* __restrict_
                 for (int t = 0; t < KT; ++t) acc[i][t] = mfma4(pv[t], rv[i], acc[i][t]);
         }
         __syncthreads();
+    };
+    fetch(rq[0], pq[0], 0);
+    fetch(rq[1], pq[1], 1);
+    fetch(rq[2], pq[2], 2);
+    for (int64_t st = 0; st < nst; st += 3) {
+        stage(rq[0], pq[0], st);
+        if (st + 1 >= nst) break;
+        stage(rq[1], pq[1], st + 1);
+        if (st + 2 >= nst) break;
+        stage(rq[2], pq[2], st + 2);
     }
     // acc[i][t] lane: Q^T row 16 t + 4 lg + v, column c0 + 64 w + 4 li + i
     float* qtb = qt + b * kp * n;
@@ -668,6 +683,28 @@ __device__ __forceinline__ float factor_at(const void* f, const float* scales, i
     }
 }
 
+// The same value, written so that a batch of them issues every load before any is
+// used: the index is clamped into range and the value is multiplied by 1 or 0
+// afterwards.  (A select on the loaded value would be turned back into a branch
+// around the load; the product cannot be, and a dropped entry becomes +-0, which
+// leaves every sum it enters unchanged because the sums start at +0.)
+template <int FB>
+__device__ __forceinline__ float factor_sel(const void* f, const float* scales, int64_t row, int k, int kk,
+                                            bool keep) {
+    const int kc = kk < k ? kk : k - 1;
+    float x;
+    if constexpr (FB == 4) {
+        const uint8_t byte = static_cast<const uint8_t*>(f)[(row * k + kc) >> 1];
+        const int nib = (kc & 1) ? (byte >> 4) : (byte & 0xF);
+        x = static_cast<float>(nib >= 8 ? nib - 16 : nib) * scales[kc];
+    } else if constexpr (FB == 16) {
+        x = __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(f)[row * k + kc]) << 16);
+    } else {
+        x = static_cast<const float*>(f)[row * k + kc];
+    }
+    return x * (keep && kk < k ? 1.0f : 0.0f);
+}
+
 template <bool HAS_E, typename ActT, int FB, int KS>
 __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__ a, float* __restrict__ ahat,
                                                          float* __restrict__ err, const void* __restrict__ u,
@@ -698,18 +735,29 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     const int64_t nrows = r0 + kRecRows < m ? kRecRows : m - r0;  // multiple of 16
     const int nst = static_cast<int>(nrows / kStage);
 
-    for (int e = threadIdx.x; e < kRecRows * 4 * KS; e += 256) {
+    // U^ rows of this workgroup (2 KS values per thread) and the V^ operands of this
+    // wave's 4 column tiles (k-slice s: V^[col][4 s + lg]), each a batch of loads issued
+    // together; rows and columns past the tensor are clamped and read as 0.
+    constexpr int kUPT = kRecRows * 4 * KS / 256;
+    float uvals[kUPT];
+#pragma unroll
+    for (int j = 0; j < kUPT; ++j) {
+        const int e = threadIdx.x + 256 * j;
         const int rr = e / (4 * KS), kk = e % (4 * KS);
-        uh[rr][kk] = rr < nrows ? factor_at<FB>(ub, usb, r0 + rr, k, kk) : 0.0f;
+        uvals[j] = factor_sel<FB>(ub, usb, r0 + (rr < nrows ? rr : nrows - 1), k, kk, rr < nrows);
     }
-    // V^ operands of this wave's 4 column tiles, k-slice s: V^[col][4 s + lg].
     const int64_t wc0 = c0 + 64 * wave;
     float av[4][KS];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int64_t col = wc0 + 16 * it + li;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) av[it][s] = col < n ? factor_at<FB>(vb, vsb, col, k, 4 * s + lg) : 0.0f;
+        for (int s = 0; s < KS; ++s) av[it][s] = factor_sel<FB>(vb, vsb, col < n ? col : n - 1, k, 4 * s + lg, col < n);
+    }
+#pragma unroll
+    for (int j = 0; j < kUPT; ++j) {
+        const int e = threadIdx.x + 256 * j;
+        uh[e / (4 * KS)][e % (4 * KS)] = uvals[j];
     }
 
     const int64_t mn = m * n;
@@ -726,6 +774,46 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
             if constexpr (HAS_E) xq[q] = cok ? RA::load(a, off) : RA::zero();
         }
     };
+    if (nrows == kRecRows && c0 + kRecCols <= n) {
+        // Whole tile: the stages run as straight-line code with loads two stages ahead
+        // and no branch around any memory operation, so each stage waits for exactly
+        // its own loads and never for the stores before them.
+        vf4 hb[2][4];
+        typename RA::T xb[2][4];
+        auto fill = [&](vf4 (&h)[4], typename RA::T (&x)[4], int st) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t off = b * mn + (r0 + kStage * st + 4 * wave + q) * n + col;
+                h[q] = ld4_nt(ahat + off);
+                if constexpr (HAS_E) x[q] = RA::load(a, off);
+            }
+        };
+        fill(hb[0], xb[0], 0);
+        fill(hb[1], xb[1], 1);
+        __syncthreads();  // uh is complete
+#pragma unroll
+        for (int st = 0; st < kNS; ++st) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                vf4 acc = vf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s) acc = mfma4(av[it][s], uh[kStage * st + li][4 * s + lg], acc);
+                *reinterpret_cast<vf4*>(&tile[li][64 * wave + 16 * it + 4 * lg]) = acc;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rr = 4 * wave + q;
+                const int64_t off = b * mn + (r0 + kStage * st + rr) * n + col;
+                const vf4 hn = hb[st & 1][q] + *reinterpret_cast<const vf4*>(&tile[rr][4 * lane]);
+                st4_nt(ahat + off, hn);
+                if constexpr (HAS_E) st4_nt(err + off, RA::cvt(xb[st & 1][q]) - hn);
+            }
+            if (st + 2 < kNS) fill(hb[st & 1], xb[st & 1], st + 2);
+            __syncthreads();
+        }
+        return;
+    }
     load_stage(0);
     __syncthreads();  // uh is complete
     for (int st = 0; st < nst; ++st) {

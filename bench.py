@@ -307,7 +307,9 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, w
     step_elems = wl.slots * numel
 
     def on(name):
-        return not want or any(name.startswith(w) for w in want)
+        # a row runs when a wanted prefix matches it; a group gate also runs when the
+        # wanted prefix names one of its rows
+        return not want or any(name.startswith(w) or w.startswith(name) for w in want)
 
     def row(name, ms, bytes_key, elems=step_elems):
         gbs_act = elems * 2 / (ms / 1e3) / 1e9
