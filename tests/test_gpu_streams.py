@@ -1,0 +1,66 @@
+"""Calls on different streams with disjoint buffers may run concurrently (C ABI
+convention): the same work issued on two streams, interleaved call by call, gives
+bit-identical results to running it on one stream."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+from gpu_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cf():
+    from activation_residual_compression_cf_amd import cf as _cf
+
+    return _cf
+
+
+def _state(cf, dev, A0, n):
+    ah = torch.empty(n, dtype=torch.float32, device=dev)
+    er = torch.empty_like(ah)
+    cf.init_state(A0, ah, er)
+    return ah, er
+
+
+def test_two_streams_match_one_stream(cf):
+    dev = cf.require_device()
+    wl = gen.Workload("streams", 512, 3072, 4, 4, "bf16", True)
+    tr = gen.Trajectory(wl, 21)
+    A = [to_dev(tr.next(), dev) for _ in range(wl.steps)]
+    n = A[0].numel()
+    say("two streams vs one stream: 1-bit, 2-bit, top-k and low rank interleaved")
+    q0 = torch.from_numpy(np.stack([gen.start_basis(21, s, 3072, 8) for s in range(4)])).to(dev)
+    results = []
+    for streams in (1, 2):
+        ss = [torch.cuda.Stream() for _ in range(streams)]
+        for s in ss:
+            s.wait_stream(torch.cuda.current_stream())
+        pick = lambda i: ss[i % streams]
+        s1, s2, sk, sl = (_state(cf, dev, A[0].reshape(-1), n) for _ in range(4))
+        ql = q0.clone()
+        ws = torch.empty(cf.lowrank_workspace_bytes(512, 3072, 8, 4), dtype=torch.uint8, device=dev)
+        c1 = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+        sc1 = torch.empty(n // 128, dtype=torch.float32, device=dev)
+        c2 = torch.empty(n // 4, dtype=torch.uint8, device=dev)
+        sc2 = torch.empty(n // 128, dtype=torch.float32, device=dev)
+        ik = torch.empty(n // 128 * 12, dtype=torch.uint8, device=dev)
+        vk = torch.empty(n // 128 * 12, dtype=torch.int16, device=dev)
+        # every buffer is allocated up front: nothing a side stream writes is freed and
+        # handed out again by the caching allocator while that stream may still use it
+        pay = cf.lowrank_payload(4, 512, 3072, 8, 4, dev)
+        for t in range(1, wl.steps):
+            a = A[t].reshape(-1)
+            cf.compress(1, a, s1[0], s1[1], c1, sc1, stream=pick(0))
+            cf.compress(2, a, s2[0], s2[1], c2, sc2, stream=pick(1))
+            cf.topk_compress(12, a, sk[0], sk[1], ik, vk, stream=pick(2))
+            cf.lowrank_compress(A[t], sl[0].view(4, 512, 3072), sl[1].view(4, 512, 3072), ql, 8, 2, 4,
+                                payload=pay, workspace=ws, stream=pick(3))
+        torch.cuda.synchronize()
+        results.append([x.clone() for x in (*s1, c1, sc1, *s2, c2, sc2, *sk, ik, vk, *sl, ql, *pay)])
+    for x, y in zip(*results):
+        assert torch.equal(x, y)
