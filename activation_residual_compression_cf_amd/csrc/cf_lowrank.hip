@@ -37,15 +37,13 @@
 // Every reduction has a fixed order; there are no atomics.
 
 #include "cf_internal.h"
+#include "cf_vec.h"
 
 namespace cf {
 namespace {
 
-typedef float vf4 __attribute__((ext_vector_type(4)));
-typedef unsigned vu2 __attribute__((ext_vector_type(2)));
-
 constexpr int kSegCols = 512;   // columns per projection segment
-constexpr int kProjRows = 256;  // rows per projection workgroup (4 waves x 64)
+constexpr int kProjRows = 256;  // rows per projection workgroup (16 stages of 16)
 constexpr int kBackCols = 256;  // columns per back-projection workgroup
 constexpr int kRecRows = 32;    // reconstruction workgroup: 32 rows x 256 columns
 constexpr int kRecCols = 256;
@@ -54,19 +52,6 @@ __device__ __forceinline__ vf4 mfma4(float a, float b, vf4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ vf4 ld4(const float* p) { return *reinterpret_cast<const vf4*>(p); }
-__device__ __forceinline__ vf4 ld4_nt(const float* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
-}
-__device__ __forceinline__ void st4_nt(float* p, vf4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<vf4*>(p));
-}
-__device__ __forceinline__ vf4 act4(const uint16_t* a, int64_t off) {
-    const vu2 w = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(a + off));
-    return vf4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-}
-__device__ __forceinline__ vf4 act4(const float* a, int64_t off) { return ld4_nt(a + off); }
-
 // Activation loads kept raw until use, so a prefetch does not wait for its data.
 template <typename ActT>
 struct RawAct;
@@ -85,7 +70,7 @@ struct RawAct<uint16_t> {
 template <>
 struct RawAct<float> {
     using T = vf4;
-    static __device__ __forceinline__ vf4 load(const float* a, int64_t off) { return ld4_nt(a + off); }
+    static __device__ __forceinline__ vf4 load(const float* a, int64_t off) { return ld_nt(a + off); }
     static __device__ __forceinline__ vf4 zero() { return vf4{0.f, 0.f, 0.f, 0.f}; }
     static __device__ __forceinline__ vf4 cvt(vf4 w) { return w; }
 };
@@ -165,7 +150,7 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
                 const bool ok = col < n;
                 if constexpr (FIRST) {
                     pa[q][h] = ok ? RA::load(a, off) : RA::zero();
-                    ph[q][h] = ok ? ld4_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
+                    ph[q][h] = ok ? ld_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
                 } else {
                     ph[q][h] = ok ? ld4(r + off) : vf4{0.f, 0.f, 0.f, 0.f};
                 }
@@ -183,7 +168,7 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
                 vf4 x = ph[q][h];
                 if constexpr (FIRST) {
                     x = RA::cvt(pa[q][h]) - x;
-                    if (c0 + cc < n) st4_nt(r + b * mn + (sr + rr) * n + c0 + cc, x);
+                    if (c0 + cc < n) st_nt(r + b * mn + (sr + rr) * n + c0 + cc, x);
                 }
                 *reinterpret_cast<vf4*>(&slab[rr][cc]) = x;
             }
@@ -770,7 +755,7 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int64_t off = b * mn + (r0 + kStage * st + 4 * wave + q) * n + col;
-            hq[q] = cok ? ld4_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
+            hq[q] = cok ? ld_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
             if constexpr (HAS_E) xq[q] = cok ? RA::load(a, off) : RA::zero();
         }
     };
@@ -784,7 +769,7 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t off = b * mn + (r0 + kStage * st + 4 * wave + q) * n + col;
-                h[q] = ld4_nt(ahat + off);
+                h[q] = ld_nt(ahat + off);
                 if constexpr (HAS_E) x[q] = RA::load(a, off);
             }
         };
@@ -806,8 +791,8 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
                 const int rr = 4 * wave + q;
                 const int64_t off = b * mn + (r0 + kStage * st + rr) * n + col;
                 const vf4 hn = hb[st & 1][q] + *reinterpret_cast<const vf4*>(&tile[rr][4 * lane]);
-                st4_nt(ahat + off, hn);
-                if constexpr (HAS_E) st4_nt(err + off, RA::cvt(xb[st & 1][q]) - hn);
+                st_nt(ahat + off, hn);
+                if constexpr (HAS_E) st_nt(err + off, RA::cvt(xb[st & 1][q]) - hn);
             }
             if (st + 2 < kNS) fill(hb[st & 1], xb[st & 1], st + 2);
             __syncthreads();
@@ -840,8 +825,8 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
                 const int rr = 4 * wave + q;
                 const int64_t off = b * mn + (r0 + kStage * st + rr) * n + col;
                 const vf4 hn = hc[q] + *reinterpret_cast<const vf4*>(&tile[rr][4 * lane]);
-                st4_nt(ahat + off, hn);
-                if constexpr (HAS_E) st4_nt(err + off, RA::cvt(xc[q]) - hn);
+                st_nt(ahat + off, hn);
+                if constexpr (HAS_E) st_nt(err + off, RA::cvt(xc[q]) - hn);
             }
         }
         __syncthreads();
