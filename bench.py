@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "compress+EF GB/s of bf16 activation per GPU; % of HBM peak (FLUX shard)"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_FP32_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 # algorithmic bytes per element: a (bf16) read, ahat read + write, err write, codes, scales
 BYTES_PER_ELEM = {
     "compress1": 2 + 4 + 4 + 4 + 1 / 8 + 4 / 128,
@@ -107,7 +108,9 @@ def cpu_baseline(wl, host_steps, bits, threads):
     import numpy as np
 
     import oracle
+    from gen import as_f32, start_basis
 
+    gen_f32 = lambda x: as_f32(x).astype(np.float32).copy()
     O = oracle.default()
     S = wl.slots
     ahat = np.empty((S, wl.m, wl.n), np.float32)
@@ -133,6 +136,17 @@ def cpu_baseline(wl, host_steps, bits, threads):
     t1 = time.perf_counter()
     O.compress(bits, host_steps[1][0], a1, e1)
     dt1 = time.perf_counter() - t1
+    # low rank: one tensor, one compressed step, single thread, per configuration
+    lowrank = {}
+    for rank, iters in ((32, 2), (8, 10)):
+        ah = gen_f32(host_steps[0][0])
+        er = np.zeros_like(ah)
+        q = start_basis(0, 0, wl.n, rank).copy()
+        t2 = time.perf_counter()
+        O.lowrank_compress(np.ascontiguousarray(host_steps[1][0]), ah, er, q, rank, iters, 4)
+        dt2 = time.perf_counter() - t2
+        lowrank[f"r{rank}_q{iters}_int4"] = {"ms_per_tensor": round(dt2 * 1e3, 1),
+                                             "GBs": round(wl.m * wl.n * 2 / dt2 / 1e9, 5)}
     return {
         "value": round(elems * 2 / dt / 1e9, 3),
         "unit": "GB/s",
@@ -141,6 +155,7 @@ def cpu_baseline(wl, host_steps, bits, threads):
         "sample": f"{nsteps} compressed steps x {S} tensors of {wl.m}x{wl.n} bf16 "
                   f"(Compact-{bits}bit, one tensor per task), {dt:.2f} s wall",
         "single_thread_GBs": round(wl.m * wl.n * 2 / dt1 / 1e9, 4),
+        "lowrank_single_thread": lowrank,
     }
 
 
@@ -183,7 +198,7 @@ def main():
     tr = gen.Trajectory(wl, args.seed)
     steps_d = []
     host_keep = []
-    n_host = 4  # steps kept on the host for the oracle baseline
+    n_host = 8  # steps kept on the host for the oracle baseline (7 compressed: ~16 s of CPU work)
     for t in range(n_gen):
         a = tr.next()
         if t < n_host:
@@ -215,12 +230,17 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start = stamp()
+    marks = [start]
     for i in range(args.steps):
         slab.compress(step_input(args.warmup + i), per_call)
-    end = stamp()
+        marks.append(stamp())
+    end = marks[-1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = start.elapsed_time(end)
+    step_ms = sorted(x.elapsed_time(y) for x, y in zip(marks, marks[1:]))
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (
+        step_ms[len(step_ms) // 2 - 1] + step_ms[len(step_ms) // 2])
     ms_per_step = total_ms / args.steps
     step_bytes_act = wl.slots * numel * 2
     value = step_bytes_act / (ms_per_step / 1e3) / 1e9
@@ -275,6 +295,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(median_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -444,6 +465,7 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
         rows[name] = {"ms_per_step": round(ms, 4), "act_GBs": round(step_elems * 2 / (ms / 1e3) / 1e9, 1),
                       "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
                       "tflops": round(step_elems * fpe / (ms / 1e3) / 1e12, 2),
+                      "mfma_fp32_frac": round(step_elems * fpe / (ms / 1e3) / 1e12 / MFMA_FP32_TFLOPS, 4),
                       "bytes_per_elem": bpe, "flops_per_elem": fpe,
                       "payload_bytes_per_tensor": wl.m * rank // 2 + wl.n * rank // 2 + 8 * rank}
         log(f"{name}: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM, "
