@@ -76,9 +76,19 @@ def _check(fn: str, rc: int):
 def _ptr(t: torch.Tensor | None):
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError("libcf takes device tensors (a host pointer would fault the kernel)")
     if not t.is_contiguous():
         raise ValueError("libcf needs contiguous tensors")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(name: str, t: torch.Tensor | None, nbytes: int, valid: bool = True):
+    """The C ABI cannot see buffer sizes: refuse a buffer smaller than the call uses.
+    With ``valid`` False (an argument the C ABI rejects anyway) nothing is checked, so
+    the call reports the library's own status."""
+    if valid and t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} B, the call needs {nbytes} B")
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -141,6 +151,9 @@ def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
         codes = torch.empty(max(n * bits // 8, 0), dtype=torch.uint8, device=a.device)
     if scales is None:
         scales = torch.empty(max(n // GROUP, 0), dtype=torch.float32, device=a.device)
+    for nm, t, nb in (("ahat", ahat, 4 * n), ("err", err, 4 * n), ("codes", codes, n * bits // 8),
+                      ("scales", scales, 4 * (n // GROUP))):
+        _need(nm, t, nb, bits in (1, 2))
     _check("cf_compress", lib.cf_compress(bits, _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
                                           _ptr(codes), _ptr(scales), n, _stream(stream)))
     return codes, scales
@@ -150,6 +163,9 @@ def decompress(bits: int, codes: torch.Tensor, scales: torch.Tensor, ahat: torch
                stream=None, out_bf16: torch.Tensor | None = None):
     """Receiver step: ahat += decoded residual; with out_bf16 (a bfloat16 tensor of the
     same size) also writes the updated reconstruction rounded to bf16."""
+    n = ahat.numel()
+    _need("codes", codes, n * bits // 8, bits in (1, 2))
+    _need("scales", scales, 4 * (n // GROUP), bits in (1, 2))
     if out_bf16 is None:
         _check("cf_decompress", lib.cf_decompress(bits, _ptr(codes), _ptr(scales), _ptr(ahat),
                                                   ahat.numel(), _stream(stream)))
@@ -169,6 +185,9 @@ def compress_ablation(mode: int, bits: int, a: torch.Tensor, ahat: torch.Tensor,
         codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=a.device)
     if scales is None:
         scales = torch.empty(n // GROUP, dtype=torch.float32, device=a.device)
+    for nm, t, nb in (("ahat", ahat, 4 * n), ("a_prev", a_prev, n * a.element_size()),
+                      ("codes", codes, n * bits // 8), ("scales", scales, 4 * (n // GROUP))):
+        _need(nm, t, nb, bits in (1, 2))
     _check("cf_compress_ablation", lib.cf_compress_ablation(
         mode, bits, _act_dtype(a), _ptr(a), _ptr(a_prev), _ptr(ahat), _ptr(codes), _ptr(scales), n,
         _stream(stream)))
@@ -183,20 +202,25 @@ def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor
         idx = torch.empty(slots, dtype=torch.uint8, device=a.device)
     if vals is None:
         vals = torch.empty(slots, dtype=torch.int16, device=a.device)
+    n = a.numel()
+    for nm, t, nb in (("ahat", ahat, 4 * n), ("err", err, 4 * n), ("idx", idx, slots), ("vals", vals, 2 * slots)):
+        _need(nm, t, nb, 1 <= k <= GROUP)
     _check("cf_topk_compress", lib.cf_topk_compress(k, _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
                                                     _ptr(idx), _ptr(vals), a.numel(), _stream(stream)))
     return idx, vals
 
 
 def topk_decompress(k: int, idx: torch.Tensor, vals: torch.Tensor, ahat: torch.Tensor, stream=None):
+    """Receiver step: ahat[group, idx] += bf16 value, for every sent slot."""
+    slots = max(ahat.numel() // GROUP * k, 0)
+    _need("idx", idx, slots, 1 <= k <= GROUP)
+    _need("vals", vals, 2 * slots, 1 <= k <= GROUP)
     _check("cf_topk_decompress", lib.cf_topk_decompress(k, _ptr(idx), _ptr(vals), _ptr(ahat), ahat.numel(),
                                                         _stream(stream)))
 
 
 def _dev_ptr(t: torch.Tensor) -> int:
-    if not t.is_contiguous():
-        raise ValueError("libcf needs contiguous tensors")
-    return t.data_ptr()
+    return _ptr(t).value
 
 
 class Slab:
@@ -226,6 +250,8 @@ class Slab:
             yield i, min(per_call, self.count - i)
 
     def init(self, a: torch.Tensor, per_call: int = 2, stream=None):
+        if a.numel() != self.count * self.numel:
+            raise ValueError("activation slab has the wrong size")
         dt, s = _act_dtype(a), _stream(stream)
         ab, esz = _dev_ptr(a), a.element_size()
         hb = _dev_ptr(self.ahat)
@@ -265,6 +291,8 @@ class Slab:
 
     def decompress(self, codes: torch.Tensor, scales: torch.Tensor, per_call: int = 2, stream=None):
         s, bits, n = _stream(stream), self.bits, self.numel
+        _need("codes", codes, self.count * n * bits // 8)
+        _need("scales", scales, 4 * self.count * (n // GROUP))
         cb, sb, hb = _dev_ptr(codes), _dev_ptr(scales), _dev_ptr(self.ahat)
         cbytes, ng = n * bits // 8, n // GROUP
         f = lib.cf_decompress
@@ -293,6 +321,18 @@ def lowrank_payload(batch: int, m: int, n: int, rank: int, factor_bits: int, dev
             torch.empty(batch * n * rank, dtype=dt, device=device), None)
 
 
+def _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload):
+    u, us, v, vs = payload
+    esz = {4: 0.5, 16: 2, 32: 4}.get(factor_bits)
+    if esz is None or rank < 1:
+        return  # the C ABI rejects these arguments itself
+    _need("u", u, int(batch * m * rank * esz))
+    _need("v", v, int(batch * n * rank * esz))
+    if factor_bits == 4:
+        _need("u_scales", us, 4 * batch * rank)
+        _need("v_scales", vs, 4 * batch * rank)
+
+
 def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
                      q_state: torch.Tensor, rank: int, iters: int, factor_bits: int = 4,
                      payload=None, workspace: torch.Tensor | None = None, stream=None):
@@ -305,6 +345,10 @@ def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
     need = lowrank_workspace_bytes(m, n, rank, batch)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+    _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload)
+    numel = batch * m * n
+    for nm, t, nb in (("ahat", ahat, 4 * numel), ("err", err, 4 * numel), ("q_state", q_state, 4 * batch * n * rank)):
+        _need(nm, t, nb, rank >= 1)
     _check("cf_lowrank_compress", lib.cf_lowrank_compress(
         _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err), m, n, rank, iters, factor_bits, batch,
         _ptr(q_state), _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _ptr(workspace),
@@ -316,6 +360,7 @@ def lowrank_decompress(factor_bits: int, payload, ahat: torch.Tensor, rank: int,
     """Receiver step on a (batch, m, n) reconstruction: ahat += U^ V^^T."""
     batch, m, n = ahat.shape
     u, us, v, vs = payload
+    _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload)
     _check("cf_lowrank_decompress", lib.cf_lowrank_decompress(
         factor_bits, _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _ptr(ahat), m, n, rank, batch,
         _stream(stream)))

@@ -220,3 +220,19 @@ def test_topk_validation(L):
     assert dec(v=0x500001) == CF_E_ALIGN
     assert dec(i=0x200000 + 1280 * 4 - 1) == CF_E_ALIAS       # idx overlapping the output mirror
     assert dec() == CF_E_DEVICE
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes device pointers only: a host tensor is refused before any call
+    (its address would fault a kernel)."""
+    import torch
+
+    from activation_residual_compression_cf_amd import cf
+
+    a = torch.zeros(256, dtype=torch.bfloat16)
+    ah = torch.zeros(256)
+    er = torch.zeros(256)
+    with pytest.raises(ValueError, match="device tensors"):
+        cf.compress(1, a, ah, er, torch.zeros(32, dtype=torch.uint8), torch.zeros(2))
+    with pytest.raises(ValueError, match="device tensors"):
+        cf.topk_compress(4, a, ah, er, torch.zeros(8, dtype=torch.uint8), torch.zeros(8, dtype=torch.int16))

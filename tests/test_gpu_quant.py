@@ -198,6 +198,10 @@ def test_failed_call_writes_nothing(cf, dev):
         cf.compress(3, a, ah, er, codes, sc)
     with pytest.raises(cf.CFError):
         cf.compress(1, a[:1000], ah[:1000], er[:1000], codes, sc)  # not a multiple of 128
+    with pytest.raises(ValueError):
+        cf.compress(2, a, ah, er, codes, sc)  # 2-bit codes need twice the bytes: refused by the binding
+    with pytest.raises(ValueError):
+        cf.decompress(1, codes[:64], sc, ah)  # codes too short for ahat
     torch.cuda.synchronize()
     for x, y in zip((ah, er, codes, sc), snap):
         assert torch.equal(x, y)
