@@ -229,17 +229,31 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
     const int tid = threadIdx.x;
     const float* yb = ypart + b * nseg * m * kp;
     float* pb = p + b * m * kp;
-    for (int e = tid; e < GR * kp; e += 256) {
-        const int rr = e / kp, kk = e % kp;
-        const int64_t row = r0 + rr;
-        double y = 0.0;
-        if (row < m) {
-            float s = yb[row * kp + kk];
-            for (int64_t q = 1; q < nseg; ++q) s = s + yb[(q * m + row) * kp + kk];
-            pb[row * kp + kk] = s;
-            y = static_cast<double>(s);
+    // Y = sum of the segment partials in segment order.  Segments run in the outer loop
+    // so that each thread's kEPT loads of one segment are in flight together.
+    constexpr int kEPT = GR * kp / 256;
+    float ysum[kEPT];
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+        const int e = tid + 256 * j;
+        const int64_t row = r0 + e / kp < m ? r0 + e / kp : m - 1;
+        ysum[j] = yb[row * kp + e % kp];
+    }
+    for (int64_t q = 1; q < nseg; ++q) {
+#pragma unroll
+        for (int j = 0; j < kEPT; ++j) {
+            const int e = tid + 256 * j;
+            const int64_t row = r0 + e / kp < m ? r0 + e / kp : m - 1;
+            ysum[j] = ysum[j] + yb[(q * m + row) * kp + e % kp];
         }
-        ys[rr][kk] = y;
+    }
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+        const int e = tid + 256 * j;
+        const int rr = e / kp, kk = e % kp;
+        const bool in = r0 + rr < m;
+        if (in) pb[(r0 + rr) * kp + kk] = ysum[j];
+        ys[rr][kk] = in ? static_cast<double>(ysum[j]) : 0.0;
     }
     __syncthreads();
     const int ti = tid >> 4, tj = tid & 15;
@@ -266,8 +280,11 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
         for (int j = 0; j < KT; ++j) gp[(ti * KT + i) * kp + tj * KT + j] = g[i][j];
 }
 
+// Threads per tensor of the factorisation (one workgroup per tensor).
+constexpr int kCholThreads = 256;
+
 template <int KT>
-__global__ __launch_bounds__(256) void k_lr_chol(const double* __restrict__ gpart, double* __restrict__ xinv,
+__global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restrict__ gpart, double* __restrict__ xinv,
                                                   int* __restrict__ alive, int64_t gblocks, int k) {
     constexpr int kp = 16 * KT;
     __shared__ double G[kp][kp + 1];  // Gram, then L in its lower triangle
@@ -276,11 +293,29 @@ __global__ __launch_bounds__(256) void k_lr_chol(const double* __restrict__ gpar
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const double* gb = gpart + b * gblocks * kp * kp;
-    for (int e = tid; e < kp * kp; e += 256) {
-        double s = gb[e];
-        for (int64_t q = 1; q < gblocks; ++q) s += gb[q * kp * kp + e];
-        G[e / kp][e % kp] = s;
-        X[e / kp][e % kp] = (e / kp == e % kp) ? 1.0 : 0.0;
+    // G = sum of the block Grams in block order; blocks in the outer loop so that each
+    // thread's loads of one block are in flight together
+    constexpr int kEPT = (kp * kp + kCholThreads - 1) / kCholThreads;
+    double gs[kEPT];
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+        const int e = tid + kCholThreads * j;
+        gs[j] = e < kp * kp ? gb[e] : 0.0;
+    }
+    for (int64_t q = 1; q < gblocks; ++q) {
+#pragma unroll
+        for (int j = 0; j < kEPT; ++j) {
+            const int e = tid + kCholThreads * j;
+            if (e < kp * kp) gs[j] += gb[q * kp * kp + e];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kEPT; ++j) {
+        const int e = tid + kCholThreads * j;
+        if (e < kp * kp) {
+            G[e / kp][e % kp] = gs[j];
+            X[e / kp][e % kp] = (e / kp == e % kp) ? 1.0 : 0.0;
+        }
     }
     __syncthreads();
     double tr = 0.0;
@@ -288,18 +323,19 @@ __global__ __launch_bounds__(256) void k_lr_chol(const double* __restrict__ gpar
     const double thresh = 1e-10 * tr;
     __syncthreads();  // every trace read precedes the in-place factorisation
     for (int j = 0; j < kp; ++j) {
+        // every thread derives the pivot from the same LDS value, so no barrier is
+        // needed before the column is scaled; thread 0 alone writes it back
+        const double d = G[j][j];
+        const bool dj = !(j < k && d > thresh);
+        const double piv = dj ? 0.0 : sqrt(d);
+        for (int i = j + 1 + tid; i < kp; i += kCholThreads) G[i][j] = dj ? 0.0 : G[i][j] / piv;
+        __syncthreads();
         if (tid == 0) {
-            const double d = G[j][j];
-            const bool ok = j < k && d > thresh;
-            G[j][j] = ok ? sqrt(d) : 0.0;
-            dead[j] = ok ? 0 : 1;
+            G[j][j] = piv;
+            dead[j] = dj ? 1 : 0;
         }
-        __syncthreads();
-        const bool dj = dead[j] != 0;
-        for (int i = j + 1 + tid; i < kp; i += 256) G[i][j] = dj ? 0.0 : G[i][j] / G[j][j];
-        __syncthreads();
         // trailing update of the lower triangle: G[i][l] -= L[i][j] L[l][j], j < l <= i
-        for (int e = tid; e < kp * kp; e += 256) {
+        for (int e = tid; e < kp * kp; e += kCholThreads) {
             const int i = e / kp, l = e % kp;
             if (l > j && l <= i) G[i][l] -= G[i][j] * G[l][j];
         }
@@ -308,16 +344,16 @@ __global__ __launch_bounds__(256) void k_lr_chol(const double* __restrict__ gpar
     // X = L^-1 by forward elimination on the rows of the identity
     for (int j = 0; j < kp; ++j) {
         const bool dj = dead[j] != 0;
-        for (int c = tid; c <= j; c += 256) X[j][c] = dj ? 0.0 : X[j][c] / G[j][j];
+        for (int c = tid; c <= j; c += kCholThreads) X[j][c] = dj ? 0.0 : X[j][c] / G[j][j];
         __syncthreads();
-        for (int e = tid; e < (kp - j - 1) * (j + 1); e += 256) {
+        for (int e = tid; e < (kp - j - 1) * (j + 1); e += kCholThreads) {
             const int i = j + 1 + e / (j + 1), c = e % (j + 1);
             X[i][c] -= G[i][j] * X[j][c];
         }
         __syncthreads();
     }
     double* xb = xinv + b * kp * kp;
-    for (int e = tid; e < kp * kp; e += 256) xb[e] = X[e / kp][e % kp];
+    for (int e = tid; e < kp * kp; e += kCholThreads) xb[e] = X[e / kp][e % kp];
     if (tid < kp) alive[b * kp + tid] = dead[tid] ? 0 : 1;
 }
 
@@ -884,7 +920,9 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch};
         if ((e = go(&k_lr_gram<KT>, batch * gblocks, gargs, stream)) != hipSuccess) return e;
         void* cargs[] = {(void*)&ws.gpart, (void*)&ws.xinv, (void*)&ws.alive, &gblocks, &k};
-        if ((e = go(&k_lr_chol<KT>, batch, cargs, stream)) != hipSuccess) return e;
+        if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>), dim3(static_cast<unsigned>(batch)),
+                                 dim3(kCholThreads), cargs, 0, stream)) != hipSuccess)
+            return e;
         void* sargs[] = {(void*)&ws.p, (void*)&ws.xinv, &m, &batch};
         if ((e = go(&k_lr_solve<KT>, batch * ((m + 255) / 256), sargs, stream)) != hipSuccess) return e;
         void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal};
