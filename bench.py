@@ -86,8 +86,12 @@ def counter_traffic():
     return float(b.group(1))
 
 
-def time_calls(torch, fn, reps):
-    """Mean ms per call of fn() over reps calls, each bracketed by events."""
+def time_calls(torch, fn, reps, warm=1):
+    """Mean ms per call of fn() over reps calls, each bracketed by events, after `warm`
+    untimed calls (the first launch of a kernel also loads its code object)."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
     pairs = []
     for _ in range(reps):
         a = torch.cuda.Event(enable_timing=True)
