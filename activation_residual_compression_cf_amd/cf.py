@@ -143,9 +143,10 @@ def init_state(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None = N
                                               a.numel(), _stream(stream)))
 
 
-def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
+def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None,
              codes: torch.Tensor | None = None, scales: torch.Tensor | None = None, stream=None):
-    """One sender step; returns (codes uint8[numel*bits/8], scales fp32[numel/128])."""
+    """One sender step; returns (codes uint8[numel*bits/8], scales fp32[numel/128]).
+    err None skips the (diagnostic) error buffer."""
     n = a.numel()
     if codes is None:
         codes = torch.empty(max(n * bits // 8, 0), dtype=torch.uint8, device=a.device)
@@ -194,7 +195,7 @@ def compress_ablation(mode: int, bits: int, a: torch.Tensor, ahat: torch.Tensor,
     return codes, scales
 
 
-def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
+def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None,
                   idx: torch.Tensor | None = None, vals: torch.Tensor | None = None, stream=None):
     """One top-k sender step; returns (idx uint8[numel/128*k], vals bf16 bits int16[numel/128*k])."""
     slots = max(a.numel() // GROUP * k, 0)
@@ -333,7 +334,7 @@ def _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload):
         _need("v_scales", vs, 4 * batch * rank)
 
 
-def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor,
+def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None,
                      q_state: torch.Tensor, rank: int, iters: int, factor_bits: int = 4,
                      payload=None, workspace: torch.Tensor | None = None, stream=None):
     """One low-rank sender step on a (batch, m, n) activation; returns the payload

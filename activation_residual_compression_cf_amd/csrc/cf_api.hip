@@ -111,14 +111,15 @@ int cf_init_state(int a_dtype, const void* a, float* ahat, float* err, int64_t n
 int cf_compress(int bits, int a_dtype, const void* a, float* ahat, float* err, uint8_t* codes,
                 float* scales, int64_t numel, void* stream) {
     if ((bits != 1 && bits != 2) || (a_dtype != CF_BF16 && a_dtype != CF_F32)) return CF_E_ARG;
-    if (!a || !ahat || !err || !codes || !scales) return CF_E_NULL;
+    if (!a || !ahat || !codes || !scales) return CF_E_NULL;
     if (int rc = valid_numel(numel)) return rc;
-    if (!aligned16(a) || !aligned16(ahat) || !aligned16(err) || !aligned16(codes) || !aligned4(scales))
+    if (!aligned16(a) || !aligned16(ahat) || (err && !aligned16(err)) || !aligned16(codes) ||
+        !aligned4(scales))
         return CF_E_ALIGN;
     const Range r[5] = {range_of(a, act_bytes(a_dtype, numel)), range_of(ahat, numel * 4),
-                        range_of(err, numel * 4), range_of(codes, numel * bits / 8),
+                        range_of(err, err ? numel * 4 : 0), range_of(codes, numel * bits / 8),
                         range_of(scales, numel / CF_GROUP * 4)};
-    const bool out[5] = {false, true, true, true, true};
+    const bool out[5] = {false, true, err != nullptr, true, true};
     if (any_alias(r, out)) return CF_E_ALIAS;
     if (int rc = check_device()) return rc;
     return cf::launch_compress(bits, a_dtype, a, ahat, err, codes, scales, numel,
@@ -187,14 +188,15 @@ int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const v
 int cf_topk_compress(int k, int a_dtype, const void* a, float* ahat, float* err, uint8_t* idx, uint16_t* vals,
                      int64_t numel, void* stream) {
     if (k < 1 || k > CF_GROUP || (a_dtype != CF_BF16 && a_dtype != CF_F32)) return CF_E_ARG;
-    if (!a || !ahat || !err || !idx || !vals) return CF_E_NULL;
+    if (!a || !ahat || !idx || !vals) return CF_E_NULL;
     if (int rc = valid_numel(numel)) return rc;
-    if (!aligned16(a) || !aligned16(ahat) || !aligned16(err) || (reinterpret_cast<uintptr_t>(vals) & 1u))
+    if (!aligned16(a) || !aligned16(ahat) || (err && !aligned16(err)) ||
+        (reinterpret_cast<uintptr_t>(vals) & 1u))
         return CF_E_ALIGN;
     const int64_t slots = numel / CF_GROUP * k;
     const Range r[5] = {range_of(a, act_bytes(a_dtype, numel)), range_of(ahat, numel * 4),
-                        range_of(err, numel * 4), range_of(idx, slots), range_of(vals, slots * 2)};
-    const bool out[5] = {false, true, true, true, true};
+                        range_of(err, err ? numel * 4 : 0), range_of(idx, slots), range_of(vals, slots * 2)};
+    const bool out[5] = {false, true, err != nullptr, true, true};
     if (any_alias(r, out)) return CF_E_ALIAS;
     if (int rc = check_device()) return rc;
     return cf::launch_topk_compress(k, a_dtype, a, ahat, err, idx, vals, numel,
@@ -235,11 +237,11 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
     if (a_dtype != CF_BF16 && a_dtype != CF_F32) return CF_E_ARG;
     if (factor_bits != 4 && factor_bits != 16 && factor_bits != 32) return CF_E_ARG;
     if (iters < 1 || iters > 64) return CF_E_ARG;
-    if (!a || !ahat || !err || !q_state || !u || !v || !workspace) return CF_E_NULL;
+    if (!a || !ahat || !q_state || !u || !v || !workspace) return CF_E_NULL;
     if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
     const size_t need = cf_lowrank_workspace_bytes(m, n, rank, batch);
     if (need == 0 || (factor_bits == 4 && (rank & 1))) return CF_E_SHAPE;
-    if (!aligned16(a) || !aligned16(ahat) || !aligned16(err) || !aligned4(q_state) ||
+    if (!aligned16(a) || !aligned16(ahat) || (err && !aligned16(err)) || !aligned4(q_state) ||
         !aligned4(u) || !aligned4(v) || (u_scales && !aligned4(u_scales)) ||
         (v_scales && !aligned4(v_scales)) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return CF_E_ALIGN;
@@ -248,13 +250,13 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
     const int64_t fsz = factor_bits / 4;  // factor bytes per (row, rank) pair, times 2
     const Range r[8] = {range_of(a, act_bytes(a_dtype, numel)),
                         range_of(ahat, numel * 4),
-                        range_of(err, numel * 4),
+                        range_of(err, err ? numel * 4 : 0),
                         range_of(q_state, int64_t(batch) * n * rank * 4),
                         range_of(u, int64_t(batch) * m * rank * fsz / 2),
                         range_of(v, int64_t(batch) * n * rank * fsz / 2),
                         range_of(u_scales, factor_bits == 4 ? int64_t(batch) * rank * 4 : 0),
                         range_of(v_scales, factor_bits == 4 ? int64_t(batch) * rank * 4 : 0)};
-    const bool out[8] = {false, true, true, true, true, true, factor_bits == 4, factor_bits == 4};
+    const bool out[8] = {false, true, err != nullptr, true, true, true, factor_bits == 4, factor_bits == 4};
     if (any_alias(r, out)) return CF_E_ALIAS;
     const Range wsr = range_of(workspace, static_cast<int64_t>(need));
     for (const Range& x : r)

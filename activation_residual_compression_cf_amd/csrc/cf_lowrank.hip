@@ -942,6 +942,9 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     const float* usc = u_scales;
     const float* vsc = v_scales;
     void* rargs[] = {&a, &ahat, &err, &uc, &usc, &vc, &vsc, &m, &n, &k, &batch, &rtotal};
+    // without an error buffer the sender's reconstruction is the receiver's: ahat += U^ V^^T
+    // (a is neither read nor needed)
+    if (!err) return launch_reconstruct<false, ActT>(factor_bits, k, rtotal, rargs, stream);
     return launch_reconstruct<true, ActT>(factor_bits, k, rtotal, rargs, stream);
 }
 

@@ -155,7 +155,9 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
         if (ok[k]) {
             const int64_t off = gi[k] * kGroup + hl * 4;
             st_nt(ahat + off, hn);
-            if constexpr (MODE == kEF) st_nt(err + off, e);
+            if constexpr (MODE == kEF) {
+                if (err) st_nt(err + off, e);  // the error buffer is optional (wave-uniform test)
+            }
             if constexpr (BITS == 1) {
                 if ((hl & 7) == 0) *reinterpret_cast<uint32_t*>(codes + gi[k] * 16 + (hl >> 1)) = w;
             } else {

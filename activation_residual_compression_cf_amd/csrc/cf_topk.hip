@@ -84,7 +84,7 @@ __device__ __forceinline__ DirectPayload direct_payload(uint8_t* idx, uint16_t* 
 }
 
 // One group on one wave: selection, state update, payload.
-template <typename RawT, typename Payload>
+template <bool HAS_E, typename RawT, typename Payload>
 __device__ __forceinline__ void topk_group(RawT raw, vf2 h, int64_t g, int lane, int k, float* __restrict__ ahat,
                                            float* __restrict__ err, const Payload& pay) {
     const vf2 x = widen_pair(raw);
@@ -117,12 +117,12 @@ __device__ __forceinline__ void topk_group(RawT raw, vf2 h, int64_t g, int lane,
     const float hn1 = sel1 ? h.y + bf16_widen(v1) : h.y;
     const int64_t off = g * kGroup + lane * 2;
     __builtin_nontemporal_store(vf2{hn0, hn1}, reinterpret_cast<vf2*>(ahat + off));
-    __builtin_nontemporal_store(vf2{x.x - hn0, x.y - hn1}, reinterpret_cast<vf2*>(err + off));
+    if constexpr (HAS_E) __builtin_nontemporal_store(vf2{x.x - hn0, x.y - hn1}, reinterpret_cast<vf2*>(err + off));
     pay.put(slot0, sel0, lane * 2, v0);
     pay.put(slot1, sel1, lane * 2 + 1, v1);
 }
 
-template <typename ActT, bool STAGED>
+template <typename ActT, bool STAGED, bool HAS_E>
 __global__ __launch_bounds__(kBlock) void k_topk_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
                                                           float* __restrict__ err, uint8_t* __restrict__ idx,
                                                           uint16_t* __restrict__ vals, int k, int64_t ngroups) {
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kBlock) void k_topk_compress(const ActT* __restrict
     if (g0 + kPerWave > ngroups) {  // ragged tail of the last wave
         for (int64_t g = g0; g < ngroups; ++g) {
             const int64_t off = g * kGroup + lane * 2;
-            topk_group(load_pair(a, off), __builtin_nontemporal_load(reinterpret_cast<const vf2*>(ahat + off)), g,
+            topk_group<HAS_E>(load_pair(a, off), __builtin_nontemporal_load(reinterpret_cast<const vf2*>(ahat + off)), g,
                        lane, k, ahat, err, direct_payload(idx, vals, g, k));
         }
         return;
@@ -160,9 +160,9 @@ __global__ __launch_bounds__(kBlock) void k_topk_compress(const ActT* __restrict
         if constexpr (STAGED) {
             const StagedPayload pay{reinterpret_cast<uint8_t*>(sidx[wave]) + j * k,
                                     reinterpret_cast<uint16_t*>(sval[wave]) + j * k};
-            topk_group(xr[j], hr[j], g0 + j, lane, k, ahat, err, pay);
+            topk_group<HAS_E>(xr[j], hr[j], g0 + j, lane, k, ahat, err, pay);
         } else {
-            topk_group(xr[j], hr[j], g0 + j, lane, k, ahat, err, direct_payload(idx, vals, g0 + j, k));
+            topk_group<HAS_E>(xr[j], hr[j], g0 + j, lane, k, ahat, err, direct_payload(idx, vals, g0 + j, k));
         }
     }
     if constexpr (STAGED) {
@@ -246,8 +246,13 @@ hipError_t run_topk(const ActT* a, float* ahat, float* err, uint8_t* idx, uint16
     const int64_t waves = (ngroups + kPerWave - 1) / kPerWave;
     const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
     const bool staged = ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(vals)) & 3u) == 0;
-    const void* fn = staged ? reinterpret_cast<const void*>(&k_topk_compress<ActT, true>)
-                            : reinterpret_cast<const void*>(&k_topk_compress<ActT, false>);
+    const void* fn;
+    if (err)
+        fn = staged ? reinterpret_cast<const void*>(&k_topk_compress<ActT, true, true>)
+                    : reinterpret_cast<const void*>(&k_topk_compress<ActT, false, true>);
+    else
+        fn = staged ? reinterpret_cast<const void*>(&k_topk_compress<ActT, true, false>)
+                    : reinterpret_cast<const void*>(&k_topk_compress<ActT, false, false>);
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), args, 0, stream);
 }
 

@@ -45,6 +45,9 @@ BYTES_PER_ELEM = {
     "topk12": 2 + 4 + 4 + 4 + 12 * 3 / 128,
     "topk6": 2 + 4 + 4 + 4 + 6 * 3 / 128,
     "topk_decode12": 4 + 4 + 12 * 3 / 128,
+    # senders without the (diagnostic) error buffer: no 4-byte e write per element
+    "compress1_noerr": 2 + 4 + 4 + 1 / 8 + 4 / 128,
+    "topk12_noerr": 2 + 4 + 4 + 12 * 3 / 128,
 }
 
 
@@ -352,6 +355,8 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, w
         lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on)
     if on("topk"):
         topk_rows(torch, cf, dev, wl, steps_d, compressed, row, on)
+    if on("noerr"):
+        noerr_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, row, rows, step_elems)
     if on("compress2_cogvideo"):
         cogvideo_row(torch, np, cf, gen, dev, per_call, row)
     if on("ef_study"):
@@ -415,6 +420,43 @@ def topk_rows(torch, cf, dev, wl, steps_d, compressed, row, on):
             del rx
         del idx, vals
     del ahat, err
+    torch.cuda.empty_cache()
+
+
+def noerr_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, row, rows, step_elems):
+    """The senders with err = NULL (the error feedback lives in ahat; the error buffer is
+    diagnostic): 1-bit and top-12 over the whole step, and low rank r32/q2."""
+    n = wl.slots * wl.numel
+    ahat = torch.empty(n, dtype=torch.float32, device=dev)
+    cf.init_state(steps_d[0], ahat)
+    codes = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 128, dtype=torch.float32, device=dev)
+    it = iter(range(10 ** 9))
+    ms = time_calls(torch, lambda: cf.compress(1, steps_d[compressed[next(it) % len(compressed)]].reshape(-1),
+                                               ahat, None, codes, scales), 8)
+    row("noerr_compress1_flux", ms, "compress1_noerr")
+    idx = torch.empty(n // 128 * 12, dtype=torch.uint8, device=dev)
+    vals = torch.empty(n // 128 * 12, dtype=torch.int16, device=dev)
+    cf.init_state(steps_d[0], ahat)
+    ms = time_calls(torch, lambda: cf.topk_compress(12, steps_d[compressed[next(it) % len(compressed)]].reshape(-1),
+                                                    ahat, None, idx, vals), 8)
+    row("noerr_topk12_flux", ms, "topk12_noerr")
+    del codes, scales, idx, vals
+    rank, iters = 32, 2
+    ah3 = ahat.view(wl.slots, wl.m, wl.n)
+    cf.init_state(steps_d[0], ah3)
+    qs = torch.from_numpy(np.stack([gen.start_basis(0, s, wl.n, rank) for s in range(wl.slots)])).to(dev)
+    ws = torch.empty(cf.lowrank_workspace_bytes(wl.m, wl.n, rank, wl.slots), dtype=torch.uint8, device=dev)
+    pay = cf.lowrank_payload(wl.slots, wl.m, wl.n, rank, 4, dev)
+    a3 = [steps_d[c].view(wl.slots, wl.m, wl.n) for c in compressed]
+    ms = time_calls(torch, lambda: cf.lowrank_compress(a3[next(it) % len(a3)], ah3, None, qs, rank, iters, 4,
+                                                       pay, ws), 4)
+    bpe = lowrank_bytes_per_elem(iters) - 6  # the reconstruction reads ahat only and writes ahat
+    hbm = step_elems * bpe / (ms / 1e3) / 1e9
+    rows["noerr_lowrank_r32_q2_int4_flux"] = {"ms_per_step": round(ms, 4), "hbm_GBs": round(hbm, 1),
+                                               "hbm_frac": round(hbm / HBM_PEAK_GBS, 4), "bytes_per_elem": bpe}
+    log(f"noerr_lowrank_r32_q2_int4_flux: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM")
+    del ahat, qs, ws, pay
     torch.cuda.empty_cache()
 
 

@@ -23,6 +23,10 @@
  *     corrupt the error feedback).
  *   - Activations `a` are bf16 (CF_BF16, raw 16-bit storage) or fp32 (CF_F32),
  *     row-major; the reconstruction `ahat` and the error buffer `err` are fp32.
+ *   - The error feedback lives in `ahat`: the next step's residual is a - ahat, so
+ *     the sender never reads `err`, and resuming needs `ahat` alone.  The senders
+ *     therefore take `err = NULL`, which skips writing it (4 bytes per element less;
+ *     the low-rank sender also skips re-reading `a`).
  *     State lives only in caller buffers, so a checkpoint is a copy of them.
  *   - A group is CF_GROUP = 128 contiguous elements; `numel` must be a positive
  *     multiple of 128.  Several tensors laid out back to back may be passed as
@@ -90,7 +94,7 @@ int cf_init_state(int a_dtype, const void* a, float* ahat, float* err, int64_t n
  *   ahat = ahat + d;   err = a - ahat        (each operation rounded once)
  *   codes: numel*bits/8 bytes, LSB first, groups back to back (16*bits bytes
  *          per group); scales: numel/128 fp32, one per group.
- *   a: in; ahat: in/out; err: out; codes, scales: out.
+ *   a: in; ahat: in/out; err: out or NULL; codes, scales: out.
  */
 int cf_compress(int bits, int a_dtype, const void* a, float* ahat, float* err, uint8_t* codes,
                 float* scales, int64_t numel, void* stream);
@@ -146,7 +150,7 @@ int cf_compress_ablation(int mode, int bits, int a_dtype, const void* a, const v
  *   1 <= k <= 128 (k = 12 spends the 2-bit budget of 36 bytes per group).
  *   idx: numel/128*k bytes, any alignment; vals: numel/128*k bf16 (raw 16-bit),
  *   2-byte aligned; a, ahat, err: 16-byte aligned.
- *   a: in; ahat: in/out; err, idx, vals: out.
+ *   a: in; ahat: in/out; err: out or NULL; idx, vals: out.
  */
 int cf_topk_compress(int k, int a_dtype, const void* a, float* ahat, float* err, uint8_t* idx, uint16_t* vals,
                      int64_t numel, void* stream);
@@ -181,7 +185,7 @@ int cf_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* a
  *   ahat = ahat + U^ V^^T;   err = a - ahat;
  *   q_state = Q (a column zeroed by the rank guard keeps its previous value).
  * Buffers (all device memory):
- *   a: batch*m*n (a_dtype), in; ahat: batch*m*n fp32, in/out; err: out;
+ *   a: batch*m*n (a_dtype), in; ahat: batch*m*n fp32, in/out; err: out or NULL;
  *   q_state: batch*n*rank fp32, in/out (the start basis; a seeded N(0,1) matrix
  *     before the first compressed step);
  *   u: batch*m*rank*factor_bits/8 bytes, out; v: batch*n*rank*factor_bits/8 bytes,

@@ -236,3 +236,22 @@ def test_binding_refuses_host_tensors():
         cf.compress(1, a, ah, er, torch.zeros(32, dtype=torch.uint8), torch.zeros(2))
     with pytest.raises(ValueError, match="device tensors"):
         cf.topk_compress(4, a, ah, er, torch.zeros(8, dtype=torch.uint8), torch.zeros(8, dtype=torch.int16))
+
+
+def test_error_buffer_is_optional_for_senders(L):
+    """err = NULL is accepted by every sender (the error feedback lives in ahat); the
+    valid calls stop at the device check."""
+    L.cf_compress.argtypes = [ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p]
+    assert L.cf_compress(1, 0, P(0x100000), P(0x200000), None, P(0x300000), P(0x400000), 1280, None) == CF_E_DEVICE
+    L.cf_topk_compress.argtypes = ([ctypes.c_int] * 2 + [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p])
+    assert L.cf_topk_compress(12, 0, P(0x100000), P(0x200000), None, P(0x400000), P(0x500000), 1280,
+                              None) == CF_E_DEVICE
+    L.cf_lowrank_workspace_bytes.restype = ctypes.c_size_t
+    L.cf_lowrank_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    need = L.cf_lowrank_workspace_bytes(64, 128, 8, 1)
+    L.cf_lowrank_compress.argtypes = ([ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64] + [ctypes.c_int] * 4 +
+                                      [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
+    assert L.cf_lowrank_compress(0, P(0x1000000), P(0x2000000), None, 64, 128, 8, 2, 4, 1, P(0x3000000),
+                                 P(0x4000000), P(0x5000000), P(0x6000000), P(0x7000000), P(0x8000000),
+                                 need, None) == CF_E_DEVICE
