@@ -38,6 +38,7 @@ BYTES_PER_ELEM = {
     "compress2": 2 + 4 + 4 + 4 + 2 / 8 + 4 / 128,
     "decode1": 4 + 4 + 1 / 8 + 4 / 128,
     "decode2": 4 + 4 + 2 / 8 + 4 / 128,
+    "decode2_bf16": 4 + 4 + 2 + 2 / 8 + 4 / 128,  # plus the bf16 copy for the attention consumer
     "init": 2 + 4 + 4,
     # top-k sender: the quantizer's 14 B of state traffic, then k index bytes and k bf16
     # values per group; receiver: the payload and one read + write of the mirror (k
@@ -384,7 +385,12 @@ def quant_rows(torch, cf, dev, wl, steps_d, compressed, per_call, row, on):
         rx.init(steps_d[0], per_call)
         ms = time_calls(torch, lambda: rx.decompress(src.codes, src.scales, per_call), 8)
         row(f"decode{bits}_flux", ms, f"decode{bits}")
-        del rx
+        # the same decode with the bf16 copy of the reconstruction, as one call for the step
+        out16 = torch.empty(wl.slots * numel, dtype=torch.bfloat16, device=dev)
+        rxf, cf_, sf_ = rx.ahat.view(-1), src.codes.view(-1), src.scales.view(-1)
+        ms = time_calls(torch, lambda: cf.decompress(bits, cf_, sf_, rxf, out_bf16=out16), 8)
+        row(f"decode{bits}_bf16_flux", ms, f"decode{bits}_bf16")
+        del rx, out16
     s1 = cf.Slab(wl.slots, numel, 1, dev)
     s1.init(steps_d[0], per_call)
     s1.compress(steps_d[compressed[0]], per_call)
