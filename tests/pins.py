@@ -488,6 +488,30 @@ def pin_payload_size(O=None):
     assert (m + n) * 8 * 2 == 65536
 
 
+# ------------------------------------------------------------ ablation modes
+def pin_ablation_relations(O):
+    """The ablation modes reduce to the main path (measured-effects table, EF ablation;
+    Surprising findings): naive quantization of a is the EF step from Ahat = 0, with the
+    decoded activation as its output; the no-EF step is the EF step from Ahat = a_prev,
+    whose decoded residual is added to the caller's mirror."""
+    traj = scaled_trajectory(16, 512, 3)
+    for bits in (1, 2):
+        a, a_prev = traj[2], traj[1]
+        out, c_n, s_n = O.quantize_naive(bits, a)
+        ah0 = np.zeros(a.shape, np.float32)
+        c_e, s_e = O.compress(bits, a, ah0, np.zeros_like(ah0))
+        assert np.array_equal(c_n, c_e) and np.array_equal(s_n, s_e)
+        assert np.array_equal(out, ah0)  # Ahat = 0 + d = d
+        mirror = f32(traj[0]) + np.float32(0.25)
+        mirror0 = mirror.copy()
+        c_x, s_x = O.compress_noef(bits, a, a_prev, mirror)
+        ahp = f32(a_prev).copy()
+        c_e, s_e = O.compress(bits, a, ahp, np.zeros_like(ahp))
+        assert np.array_equal(c_x, c_e) and np.array_equal(s_x, s_e)
+        d = decode_numpy(c_x, s_x, bits, a.size).reshape(a.shape)
+        assert np.array_equal(mirror, (mirror0 + d).astype(np.float32))
+
+
 # ---------------------------------------------------------------- top-k sparsity
 # Reading of the sparsity compressor the pages name (Limitations): per group of 128
 # keep the k residuals of largest |r| (ties to the lower index), sent in increasing

@@ -73,6 +73,14 @@ MUTANTS = [
     ("explicit_ef_error_sign", "err[base + i] = r[i] - d[i];", "err[base + i] = d[i] - r[i];"),
     ("bf16_truncates", "return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);",
      "return (uint16_t)(u >> 16);"),
+    ("noef_residual_uses_mirror",
+     "r[i] = act(dtype, a, base + i) - act(dtype, a_prev, base + i);",
+     "r[i] = act(dtype, a, base + i) - ahat[base + i];"),
+    ("noef_mirror_not_updated",
+     "for (int i = 0; i < CFO_GROUP; ++i) ahat[base + i] = ahat[base + i] + d[i];",
+     "for (int i = 0; i < CFO_GROUP; ++i) ahat[base + i] = ahat[base + i];"),
+    ("naive_input_scaled", "for (int i = 0; i < CFO_GROUP; ++i) r[i] = act(dtype, a, base + i);",
+     "for (int i = 0; i < CFO_GROUP; ++i) r[i] = 0.5f * act(dtype, a, base + i);"),
     ("topk_ties_to_higher_index", "return i < j ? -1 : (i > j);\n}\n\nstatic int by_index",
      "return i > j ? -1 : (i < j);\n}\n\nstatic int by_index"),
     ("topk_keeps_smallest", "if (ki != kj) return ki > kj ? -1 : 1;",
