@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
                     pa[q][h] = ok ? RA::load(a, off) : RA::zero();
                     ph[q][h] = ok ? ld_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
                 } else {
-                    ph[q][h] = ok ? ld4(r + off) : vf4{0.f, 0.f, 0.f, 0.f};
+                    ph[q][h] = ok ? ld_nt(r + off) : vf4{0.f, 0.f, 0.f, 0.f};
                 }
             }
     };
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
     auto fetch = [&](vf4 (&rx)[4], float (&px)[KT], int64_t st) {
         const int64_t sr = (st < nst ? st : nst - 1) * kStage;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rx[q] = ld4(rb + (sr + 4 * wave + q) * n + col);
+        for (int q = 0; q < 4; ++q) rx[q] = ld_nt(rb + (sr + 4 * wave + q) * n + col);
 #pragma unroll
         for (int j = 0; j < KT; ++j) {  // kStage * kp = 256 KT values, KT per thread
             const int e = threadIdx.x + 256 * j;
