@@ -58,6 +58,12 @@ __device__ __forceinline__ vf2 widen_pair(uint32_t w) {
 }
 __device__ __forceinline__ vf2 widen_pair(vf2 w) { return w; }
 
+// acc + the number of set bits of `mask` at lanes below this one (two mbcnt steps).
+__device__ __forceinline__ int count_below(uint64_t mask, int acc) {
+    return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), acc)));
+}
+
 // Where a group's payload goes: LDS staging slots, or the output through buffer stores.
 struct StagedPayload {
     uint8_t* idx;  // LDS, this group's k slots
@@ -90,27 +96,46 @@ __device__ __forceinline__ void topk_group(RawT raw, vf2 h, int64_t g, int lane,
     const vf2 x = widen_pair(raw);
     const float r0 = x.x - h.x, r1 = x.y - h.y;
     const uint32_t key0 = __float_as_uint(r0) & 0x7fffffffu, key1 = __float_as_uint(r1) & 0x7fffffffu;
-    // T is wave-uniform but kept in a VGPR (a plain register move the compiler cannot
-    // fold), so candidate and select stay on the vector unit.
-    uint32_t T;
+    // T and a copy of k are wave-uniform but kept in VGPRs (plain register moves the
+    // compiler cannot fold), so candidate, the "at least k" test and the select run on
+    // the vector unit and the scalar unit has only the two counts, their sum and the
+    // exact-count exit.  The scalar unit serves each SIMD every fourth cycle, so this
+    // split is what bounds a step.
+    uint32_t T, kv;
     asm volatile("v_mov_b32 %0, 0" : "=v"(T));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(kv) : "s"(k));
+    // Lowest set bit of the lane's two keys (31 for two zero keys; keys are below 2^31).
+    const uint32_t lsb = __builtin_ctz(key0 | key1 | 0x80000000u);
     if (k < kGroup) {
 #pragma unroll
         for (int b = 30; b >= 0; --b) {
+            // Once no key has a set bit at or below b, every key is a multiple of
+            // 2^(b+1) and T, decided down to bit b+1, is the k-th largest key itself:
+            // no later candidate can gain a bit.  Groups that tie at the k-th magnitude
+            // (residuals on a coarse grid) end here instead of running every bit.
+            if (b <= 19 && (b & 3) == 3 && __ballot(lsb <= static_cast<uint32_t>(b)) == 0) break;
             const uint32_t cand = T | (1u << b);
             const int cnt = __popcll(__ballot(key0 >= cand)) + __popcll(__ballot(key1 >= cand));
-            if (cnt >= k) T = cand;
+            if (cnt >= static_cast<int>(kv)) T = cand;
             if (cnt == k) break;  // exactly the keys >= T are kept
         }
     }
-    const uint64_t below = (1ull << lane) - 1ull;
-    const int above = __popcll(__ballot(key0 > T)) + __popcll(__ballot(key1 > T));
-    const int need = k - above;
-    const bool eq0 = key0 == T, eq1 = key1 == T;
-    const int eq_before = __popcll(__ballot(eq0) & below) + __popcll(__ballot(eq1) & below);
-    const bool sel0 = key0 > T || (eq0 && eq_before < need);
-    const bool sel1 = key1 > T || (eq1 && eq_before + (eq0 ? 1 : 0) < need);
-    const int slot0 = __popcll(__ballot(sel0) & below) + __popcll(__ballot(sel1) & below);
+    bool sel0 = key0 >= T, sel1 = key1 >= T;
+    const uint64_t ge0 = __ballot(sel0), ge1 = __ballot(sel1);
+    int slot0;
+    if (__popcll(ge0) + __popcll(ge1) == k) {
+        // Exactly the keys >= T are kept (most groups end the search this way).
+        slot0 = count_below(ge0, count_below(ge1, 0));
+    } else {
+        // Ties at T: the keys above T, then the lowest-indexed keys equal to T.
+        const int above = __popcll(__ballot(key0 > T)) + __popcll(__ballot(key1 > T));
+        const int need = k - above;
+        const bool eq0 = key0 == T, eq1 = key1 == T;
+        const int eq_before = count_below(__ballot(eq0), count_below(__ballot(eq1), 0));
+        sel0 = key0 > T || (eq0 && eq_before < need);
+        sel1 = key1 > T || (eq1 && eq_before + (eq0 ? 1 : 0) < need);
+        slot0 = count_below(__ballot(sel0), count_below(__ballot(sel1), 0));
+    }
     const int slot1 = slot0 + (sel0 ? 1 : 0);
     const uint32_t v0 = bf16_rne(r0), v1 = bf16_rne(r1);
     const float hn0 = sel0 ? h.x + bf16_widen(v0) : h.x;
