@@ -15,7 +15,11 @@
 
 namespace {
 
-constexpr int64_t kMaxNumel = int64_t(1) << 40;  // keeps every byte size far from overflow
+// Largest numel of one call.  The element-wise kernels launch up to one work-item per
+// 4 elements (rounded up to whole workgroups), and a dispatch counts at most
+// 2^32 - 1 work-items, so 2^33 keeps every grid well inside a dispatch (and every
+// byte size far from overflow).
+constexpr int64_t kMaxNumel = int64_t(1) << 33;
 
 struct Range {
     uintptr_t lo, hi;  // [lo, hi)
@@ -76,7 +80,7 @@ const char* cf_strerror(int status) {
     switch (status) {
         case CF_OK: return "ok";
         case CF_E_NULL: return "required pointer is NULL";
-        case CF_E_SHAPE: return "size out of range (numel must be a positive multiple of 128)";
+        case CF_E_SHAPE: return "size out of range (numel must be a positive multiple of 128, at most 2^33)";
         case CF_E_ALIGN: return "pointer misaligned (16 bytes; scales 4 bytes)";
         case CF_E_ARG: return "unsupported bits, k, dtype or mode";
         case CF_E_ALIAS: return "output range overlaps another operand";
@@ -223,7 +227,8 @@ int cf_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* a
 
 size_t cf_lowrank_workspace_bytes(int64_t m, int64_t n, int rank, int batch) {
     if (m <= 0 || n <= 0 || m % 16 || n % 16 || batch < 1 || rank < 1 || rank > cf::kMaxRank ||
-        rank > m || rank > n || m * n > kMaxNumel / batch)
+        rank > m || rank > n || m > kMaxNumel / n || m * n > kMaxNumel / batch ||
+        !cf::lowrank_launches_fit(m, n, rank, batch))
         return 0;
     size_t bytes = 0;
     cf::carve_lowrank_workspace(nullptr, m, n, rank, batch, &bytes);

@@ -10,6 +10,9 @@ namespace cf {
 // Groups of 128 contiguous elements are the unit of every 1/2-bit kernel.
 constexpr int kGroup = 128;
 
+// A dispatch counts its work-items per grid dimension in 32 bits.
+constexpr int64_t kMaxDispatchItems = (int64_t(1) << 32) - 1;
+
 hipError_t launch_init(int a_dtype, const void* a, float* ahat, float* err, int64_t numel,
                        hipStream_t stream);
 hipError_t launch_compress(int bits, int a_dtype, const void* a, float* ahat, float* err,
@@ -45,6 +48,8 @@ constexpr int kMaxRank = 64;
 // Fills the region pointers for `base` (may be null) and the total size in *bytes.
 LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch,
                                          size_t* bytes);
+// Whether every launch of one low-rank call (or of its receiver) fits a dispatch.
+bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch);
 hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m,
                                    int64_t n, int rank, int iters, int factor_bits, int64_t batch,
                                    float* q_state, void* u, float* u_scales, void* v, float* v_scales,

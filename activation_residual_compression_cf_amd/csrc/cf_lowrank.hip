@@ -209,10 +209,11 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
 //               order; right-looking Cholesky G = L L^T in LDS with the rank guard
 //               (pivot <= 1e-10 trace(G) -> dead column); X = L^-1;
 //   k_lr_solve  (batch x row blocks) P[row] = Y[row] X^T in fp64, in place over Y.
+constexpr int64_t gram_rows(int64_t kt) { return kt == 1 ? 256 : (kt == 2 ? 128 : 64); }  // rows per Gram block
 template <int KT>
 struct GramShape {
     static constexpr int kp = 16 * KT;
-    static constexpr int rows = KT == 1 ? 256 : (KT == 2 ? 128 : 64);  // rows per Gram block
+    static constexpr int rows = static_cast<int>(gram_rows(KT));
 };
 
 template <int KT>
@@ -872,6 +873,30 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
 // ------------------------------------------------------------- launchers --
 int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 
+// Workgroup counts of every launch of one call; the launches and the argument check
+// share this computation.  Every workgroup has 256 threads (kCholThreads for the
+// factorisation, one workgroup per tensor).
+struct LowrankGrids {
+    int64_t kp, nseg, gblocks;
+    int64_t prep, project, gram, chol, solve, backproject, quant, reconstruct;
+};
+
+LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
+    LowrankGrids g;
+    g.kp = (rank + 15) / 16 * 16;
+    g.nseg = (n + kSegCols - 1) / kSegCols;
+    g.gblocks = (m + gram_rows(g.kp / 16) - 1) / gram_rows(g.kp / 16);
+    g.prep = (batch * g.kp * n + 255) / 256;
+    g.project = round8(batch * ((m + kProjRows - 1) / kProjRows) * g.nseg);
+    g.gram = batch * g.gblocks;
+    g.chol = batch;
+    g.solve = batch * ((m + 255) / 256);
+    g.backproject = round8(batch * ((n + kBackCols - 1) / kBackCols));
+    g.quant = batch * ((m + 255) / 256 + (n + 255) / 256);
+    g.reconstruct = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
+    return g;
+}
+
 template <typename K>
 hipError_t go(K kernel, int64_t blocks, void** args, hipStream_t stream) {
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)), dim3(256),
@@ -900,43 +925,43 @@ template <typename ActT, int KT>
 hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_t n, int k, int iters,
                        int factor_bits, int64_t batch, float* q_state, void* u, float* u_scales, void* v,
                        float* v_scales, const LowrankWorkspace& ws, hipStream_t stream) {
+    const LowrankGrids grid = lowrank_grids(m, n, k, batch);
     int kp = 16 * KT;
-    int64_t nseg = (n + kSegCols - 1) / kSegCols;
+    int64_t nseg = grid.nseg;
     hipError_t e;
     {
-        int64_t cnt = batch * kp * n;
         void* args[] = {&q_state, (void*)&ws.qt, &n, &k, &kp, &batch};
-        if ((e = go(&k_lr_prep, (cnt + 255) / 256, args, stream)) != hipSuccess) return e;
+        if ((e = go(&k_lr_prep, grid.prep, args, stream)) != hipSuccess) return e;
     }
-    const int64_t rblocks = (m + kProjRows - 1) / kProjRows;
-    int64_t ptotal = round8(batch * rblocks * nseg);
-    int64_t btotal = round8(batch * ((n + kBackCols - 1) / kBackCols));
+    int64_t ptotal = grid.project;
+    int64_t btotal = grid.backproject;
     for (int it = 0; it < iters; ++it) {
         void* pargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &ptotal};
         e = it == 0 ? go(&k_lr_project<true, ActT, KT>, ptotal, pargs, stream)
                     : go(&k_lr_project<false, ActT, KT>, ptotal, pargs, stream);
         if (e != hipSuccess) return e;
-        int64_t gblocks = (m + GramShape<KT>::rows - 1) / GramShape<KT>::rows;
+        int64_t gblocks = grid.gblocks;
         void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch};
-        if ((e = go(&k_lr_gram<KT>, batch * gblocks, gargs, stream)) != hipSuccess) return e;
+        if ((e = go(&k_lr_gram<KT>, grid.gram, gargs, stream)) != hipSuccess) return e;
         void* cargs[] = {(void*)&ws.gpart, (void*)&ws.xinv, (void*)&ws.alive, &gblocks, &k};
-        if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>), dim3(static_cast<unsigned>(batch)),
-                                 dim3(kCholThreads), cargs, 0, stream)) != hipSuccess)
+        if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>),
+                                 dim3(static_cast<unsigned>(grid.chol)), dim3(kCholThreads), cargs, 0,
+                                 stream)) != hipSuccess)
             return e;
         void* sargs[] = {(void*)&ws.p, (void*)&ws.xinv, &m, &batch};
-        if ((e = go(&k_lr_solve<KT>, batch * ((m + 255) / 256), sargs, stream)) != hipSuccess) return e;
+        if ((e = go(&k_lr_solve<KT>, grid.solve, sargs, stream)) != hipSuccess) return e;
         void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal};
         if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
     }
     {
-        const int64_t qblocks = batch * ((m + 255) / 256 + (n + 255) / 256);
+        const int64_t qblocks = grid.quant;
         void* margs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.cmax, &m, &n};
         if ((e = go(&k_lr_colmax<KT>, qblocks, margs, stream)) != hipSuccess) return e;
         void* qargs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.cmax, (void*)&ws.alive, &m, &n, &k,
                          &factor_bits, &q_state, &u, &u_scales, &v, &v_scales};
         if ((e = go(&k_lr_pack<KT>, qblocks, qargs, stream)) != hipSuccess) return e;
     }
-    int64_t rtotal = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
+    int64_t rtotal = grid.reconstruct;
     const void* uc = u;
     const void* vc = v;
     const float* usc = u_scales;
@@ -965,8 +990,7 @@ hipError_t dispatch_rank(const ActT* a, float* ahat, float* err, int64_t m, int6
 LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch, size_t* bytes) {
     const int64_t kp = (rank + 15) / 16 * 16;
     const int64_t nseg = (n + kSegCols - 1) / kSegCols;
-    const int64_t grows = kp == 16 ? 256 : (kp == 32 ? 128 : 64);  // GramShape<kp / 16>::rows
-    const int64_t gblocks = (m + grows - 1) / grows;
+    const int64_t gblocks = lowrank_grids(m, n, rank, batch).gblocks;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t sz_r = up(batch * m * n * 4);
     const int64_t sz_qt = up(batch * kp * n * 4);
@@ -999,6 +1023,14 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
     return ws;
 }
 
+bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch) {
+    const LowrankGrids g = lowrank_grids(m, n, rank, batch);
+    const int64_t blocks[] = {g.prep, g.project, g.gram, g.solve, g.backproject, g.quant, g.reconstruct};
+    for (int64_t b : blocks)
+        if (b * 256 > kMaxDispatchItems) return false;
+    return g.chol * kCholThreads <= kMaxDispatchItems;
+}
+
 hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,
                                    int rank, int iters, int factor_bits, int64_t batch, float* q_state, void* u,
                                    float* u_scales, void* v, float* v_scales, void* workspace,
@@ -1014,7 +1046,7 @@ hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, floa
 hipError_t launch_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
                                      const float* v_scales, float* ahat, int64_t m, int64_t n, int rank,
                                      int64_t batch, hipStream_t stream) {
-    int64_t rtotal = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
+    int64_t rtotal = lowrank_grids(m, n, rank, batch).reconstruct;
     const uint16_t* a = nullptr;
     float* err = nullptr;
     int k = rank;

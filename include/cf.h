@@ -29,7 +29,7 @@
  *     the low-rank sender also skips re-reading `a`).
  *     State lives only in caller buffers, so a checkpoint is a copy of them.
  *   - A group is CF_GROUP = 128 contiguous elements; `numel` must be a positive
- *     multiple of 128.  Several tensors laid out back to back may be passed as
+ *     multiple of 128, at most 2^33.  Several tensors laid out back to back may be passed as
  *     one call (one "slab"), since no group straddles two tensors when every
  *     tensor's size is a multiple of 128.
  *   - Every pointer must be 16-byte aligned, except `scales` (one float per
@@ -59,7 +59,9 @@ enum {
     CF_E_ALIAS = -5,     /* an output range overlaps another operand */
     CF_E_WORKSPACE = -6, /* workspace missing or too small */
     CF_E_DEVICE = -7,    /* current device is not gfx950 */
-    CF_E_HIP = -8        /* the HIP runtime refused a launch */
+    CF_E_HIP = -8        /* the HIP runtime refused a launch; a call that launches several
+                            kernels (cf_lowrank_compress) may then have applied part of
+                            its update, so treat the state as lost (re-run the warmup) */
 };
 
 enum { CF_BF16 = 0, CF_F32 = 1 };
@@ -70,8 +72,8 @@ enum { CF_MODE_NOEF = 1, CF_MODE_NAIVE = 2 };
 #define CF_GROUP 128
 
 /*
- * Warmup / initialisation (measured-effects table: "1-step warmup", "2 warmup
- * steps").  During the first W steps the activation itself is sent and both
+ * Warmup / initialisation (measured-effects table: the rows with one and with two
+ * warmup steps).  During the first W steps the activation itself is sent and both
  * sides take it as their reconstruction:  ahat[i] = a[i]  and, when `err` is
  * not NULL (the sender), err[i] = 0.  The receiver passes err = NULL.
  *   a:    numel elements of `a_dtype`
@@ -122,8 +124,9 @@ int cf_decompress_bf16(int bits, const uint8_t* codes, const float* scales, floa
 
 /*
  * Ablation modes of the sender, for studies of the method's design (measured-
- * effects table: "Add residual compression with error feedback"; Surprising
- * findings: naive 1-bit compression of full activations collapses).  Same
+ * effects table: the row that adds residual compression with error feedback;
+ * Surprising findings: 1-bit quantization of whole activations, without residuals,
+ * fails).  Same
  * quantizer, codes and scales as cf_compress; per group:
  *   CF_MODE_NOEF:  r = a - a_prev (the raw step delta, no error feedback);
  *                  ahat = ahat + d (the receiver's mirror, which cf_decompress
@@ -193,9 +196,11 @@ int cf_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* a
  *   u_scales, v_scales: batch*rank fp32, out (may be NULL unless factor_bits = 4);
  *   workspace: ws_bytes >= cf_lowrank_workspace_bytes(m, n, rank, batch), 256-byte
  *     aligned; scratch, its contents are not preserved between calls.
- * Limits: m and n positive multiples of 16; 1 <= rank <= min(m, n, 64); rank even
- *   when factor_bits = 4; 1 <= iters <= 64; batch >= 1.  a, ahat, err 16-byte
- *   aligned; the other pointers 4-byte aligned.
+ * Limits: m and n positive multiples of 16; batch*m*n <= 2^33; 1 <= rank <=
+ *   min(m, n, 64); rank even when factor_bits = 4; 1 <= iters <= 64; batch >= 1;
+ *   every kernel grid within a dispatch's 2^32 - 1 work-items (only extreme shapes,
+ *   such as a single row block of 2^28 columns, reach that); CF_E_SHAPE otherwise.
+ *   a, ahat, err 16-byte aligned; the other pointers 4-byte aligned.
  * Arithmetic is fp32 (fp64 inside orth); results are deterministic.
  */
 int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,

@@ -152,8 +152,8 @@ static void quantize_group(int bits, const float* r, uint8_t* gcodes, float* sca
 
 /* ---------------------------------------------------------------------------
  * Warmup / initialisation: the first W steps send the activation itself, and
- * both sides take it as their reconstruction (measured-effects table: "1-step
- * warmup", "2 warmup steps").
+ * both sides take it as their reconstruction (measured-effects table: the rows
+ * with one and with two warmup steps).
  * ------------------------------------------------------------------------- */
 int cfo_init_state(int dtype, const void* a, float* ahat, float* err, int64_t numel) {
     if (!a || !ahat || numel < 0 || (dtype != CFO_BF16 && dtype != CFO_F32)) return CFO_EARG;

@@ -10,8 +10,8 @@ Method source throughout: "Accelerating Parallel Diffusion Model Serving with
 Residual Compression" (CompactFusion summary): section Approach (residual against the
 previous reconstruction, sender-side error feedback, low rank + INT4), the
 measured-effects table (Compact-1bit / Compact-2bit, warmup, rank 32 with INT4,
-2 vs 10 iterations), Surprising findings (naive 1-bit collapses; residual + EF stays
-close), and Experimental setup "Builds on" (error feedback from gradient compression,
+2 vs 10 iterations), Surprising findings (1-bit quantization of whole activations
+fails, residuals with EF stay close), and Experimental setup "Builds on" (error feedback from gradient compression,
 PowerSGD-style subspace iteration).
 """
 from __future__ import annotations
@@ -325,7 +325,7 @@ def pin_sender_receiver(O):
 
 def pin_2bit_beats_1bit(O):
     """2-bit tracks the trajectory more closely than 1-bit (measured-effects table),
-    and naive 1-bit of the full activation collapses (Surprising findings)."""
+    and 1-bit quantization of the whole activation fails (Surprising findings)."""
     for traj, ratio in ((tiny_trajectory(28), 0.9), (scaled_trajectory(64, 512, 28), 0.8)):
         errs = {}
         for bits in (1, 2):

@@ -87,6 +87,11 @@ def test_compress_validation(L):
     assert _compress(L, n=-128) == CF_E_SHAPE
     assert _compress(L, n=1000) == CF_E_SHAPE
     assert _compress(L, n=(1 << 40) + 128) == CF_E_SHAPE
+    # the largest call: 2^33 elements (every grid stays inside a dispatch's 2^32 - 1
+    # work-items); fake buffers 2^40 bytes apart so that none overlaps
+    T = 1 << 40
+    assert _compress(L, a=T, ah=2 * T, e=3 * T, c=4 * T, s=5 * T, n=(1 << 33) + 128) == CF_E_SHAPE
+    assert _compress(L, a=T, ah=2 * T, e=3 * T, c=4 * T, s=5 * T, n=1 << 33) == CF_E_DEVICE
     assert _compress(L, a=0x10008) == CF_E_ALIGN
     assert _compress(L, c=0x3000004) == CF_E_ALIGN
     assert _compress(L, s=0x4000002) == CF_E_ALIGN
@@ -123,6 +128,10 @@ def test_lowrank_validation(L):
     assert L.cf_lowrank_workspace_bytes(1000, 3072, 32, 1) == 0   # m not a multiple of 16
     assert L.cf_lowrank_workspace_bytes(1024, 3072, 65, 1) == 0   # rank above 64
     assert L.cf_lowrank_workspace_bytes(32, 64, 48, 1) == 0       # rank above min(m, n)
+    assert L.cf_lowrank_workspace_bytes(1024, 3072, 32, 2731) == 0  # batch*m*n above 2^33
+    # 16 x 2^28: the start-basis transpose would need 2^32 work-items in one dispatch
+    assert L.cf_lowrank_workspace_bytes(16, 1 << 28, 16, 1) == 0
+    assert L.cf_lowrank_workspace_bytes(16, 1 << 27, 16, 1) > 0
     L.cf_lowrank_compress.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 3 +
                                       [ctypes.c_int64] * 2 + [ctypes.c_int] * 4 +
                                       [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
