@@ -38,7 +38,7 @@ struct LowrankWorkspace {
     float* p;      // batch x m x kp orthonormal factor
     int* alive;    // batch x kp rank-guard flags
     double* gpart; // batch x row blocks x kp x kp Gram partials
-    double* xinv;  // batch x kp x kp inverse Cholesky factor
+    double* lfac;  // batch x kp x kp Cholesky factor, reciprocal pivots on its diagonal
     float* cmax;   // batch x row blocks x kp column maxima of the factors
 };
 

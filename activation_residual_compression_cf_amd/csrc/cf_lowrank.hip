@@ -51,6 +51,10 @@ constexpr int kRecCols = 256;
 __device__ __forceinline__ vf4 mfma4(float a, float b, vf4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+typedef double vd4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ vd4 mfma_f64(double a, double b, vd4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ vf4 ld4(const float* p) { return *reinterpret_cast<const vf4*>(p); }
 // Activation loads kept raw until use, so a prefetch does not wait for its data.
 template <typename ActT>
@@ -204,11 +208,12 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
 // orth(Y) in three launches:
 //   k_lr_gram   (batch x row blocks) Y = sum of the segment partials in segment
 //               order (fp32, written to `p` for the solve), and the fp64 Gram
-//               contribution Y_blk^T Y_blk of the block's rows;
+//               contribution Y_blk^T Y_blk of the block's rows (fp64 MFMA);
 //   k_lr_chol   (one workgroup per tensor) G = sum of the block Grams in block
 //               order; right-looking Cholesky G = L L^T in LDS with the rank guard
-//               (pivot <= 1e-10 trace(G) -> dead column); X = L^-1;
-//   k_lr_solve  (batch x row blocks) P[row] = Y[row] X^T in fp64, in place over Y.
+//               (pivot <= 1e-10 trace(G) -> dead column);
+//   k_lr_solve  (batch x row blocks) P[row] = Y[row] L^-T by forward substitution
+//               in fp64, in place over Y.
 constexpr int64_t gram_rows(int64_t kt) { return kt == 1 ? 256 : (kt == 2 ? 128 : 64); }  // rows per Gram block
 template <int KT>
 struct GramShape {
@@ -230,22 +235,29 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
     const int tid = threadIdx.x;
     const float* yb = ypart + b * nseg * m * kp;
     float* pb = p + b * m * kp;
-    // Y = sum of the segment partials in segment order.  Segments run in the outer loop
-    // so that each thread's kEPT loads of one segment are in flight together.
+    // Y = sum of the segment partials in segment order.  The loads of kSegBatch
+    // segments are issued together (indices past the last segment re-read it and are
+    // not added), so a thread waits for one batch at a time, not for every segment.
     constexpr int kEPT = GR * kp / 256;
+    constexpr int kSegBatch = 3;
     float ysum[kEPT];
+    for (int64_t q0 = 0; q0 < nseg; q0 += kSegBatch) {
+        float v[kSegBatch][kEPT];
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        const int e = tid + 256 * j;
-        const int64_t row = r0 + e / kp < m ? r0 + e / kp : m - 1;
-        ysum[j] = yb[row * kp + e % kp];
-    }
-    for (int64_t q = 1; q < nseg; ++q) {
+        for (int qq = 0; qq < kSegBatch; ++qq) {
+            const int64_t q = q0 + qq < nseg ? q0 + qq : nseg - 1;
 #pragma unroll
-        for (int j = 0; j < kEPT; ++j) {
-            const int e = tid + 256 * j;
-            const int64_t row = r0 + e / kp < m ? r0 + e / kp : m - 1;
-            ysum[j] = ysum[j] + yb[(q * m + row) * kp + e % kp];
+            for (int j = 0; j < kEPT; ++j) {
+                const int e = tid + 256 * j;
+                const int64_t row = r0 + e / kp < m ? r0 + e / kp : m - 1;
+                v[qq][j] = yb[(q * m + row) * kp + e % kp];
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < kSegBatch; ++qq) {
+            if (q0 + qq >= nseg) break;  // uniform; no memory operation below
+#pragma unroll
+            for (int j = 0; j < kEPT; ++j) ysum[j] = q0 + qq == 0 ? v[qq][j] : ysum[j] + v[qq][j];
         }
     }
 #pragma unroll
@@ -257,139 +269,146 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
         ys[rr][kk] = in ? static_cast<double>(ysum[j]) : 0.0;
     }
     __syncthreads();
-    const int ti = tid >> 4, tj = tid & 15;
-    double g[KT][KT];
-#pragma unroll
-    for (int i = 0; i < KT; ++i)
-#pragma unroll
-        for (int j = 0; j < KT; ++j) g[i][j] = 0.0;
-    for (int rr = 0; rr < GR; ++rr) {
-        double yi[KT], yj[KT];
-#pragma unroll
-        for (int i = 0; i < KT; ++i) yi[i] = ys[rr][ti * KT + i];
-#pragma unroll
-        for (int j = 0; j < KT; ++j) yj[j] = ys[rr][tj * KT + j];
-#pragma unroll
-        for (int i = 0; i < KT; ++i)
-#pragma unroll
-            for (int j = 0; j < KT; ++j) g[i][j] = fma(yi[i], yj[j], g[i][j]);
-    }
+    // G_blk = Y_blk^T Y_blk on the fp64 MFMA 16x16x4, tile by tile, 4 rows of the
+    // block per instruction.  Lane l = i + 16 s holds A[i][s] = Y[4t + s][16 ta + i] and
+    // B[s][i] = Y[4t + s][16 tb + i]; the result D[s + 4 v][i] sits in lane l, item v.
+    const int wave = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
     double* gp = gpart + (b * gblocks + blk) * kp * kp;
+    if constexpr (KT == 1) {
+        // one tile: each wave takes a quarter of the rows; partials summed in wave order
+        __shared__ double red[4][16][17];
+        vd4 acc = vd4{0.0, 0.0, 0.0, 0.0};
+        for (int t = wave * (GR / 16); t < (wave + 1) * (GR / 16); ++t) {
+            const double y = ys[4 * t + lg][li];
+            acc = mfma_f64(y, y, acc);
+        }
 #pragma unroll
-    for (int i = 0; i < KT; ++i)
+        for (int v = 0; v < 4; ++v) red[wave][lg + 4 * v][li] = acc[v];
+        __syncthreads();
+        const int i = tid >> 4, j = tid & 15;
+        gp[i * kp + j] = ((red[0][i][j] + red[1][i][j]) + red[2][i][j]) + red[3][i][j];
+    } else {
+        for (int tile = wave; tile < KT * KT; tile += 4) {
+            const int ta = tile / KT, tb = tile % KT;
+            vd4 acc = vd4{0.0, 0.0, 0.0, 0.0};
+            for (int t = 0; t < GR / 4; ++t)
+                acc = mfma_f64(ys[4 * t + lg][16 * ta + li], ys[4 * t + lg][16 * tb + li], acc);
 #pragma unroll
-        for (int j = 0; j < KT; ++j) gp[(ti * KT + i) * kp + tj * KT + j] = g[i][j];
+            for (int v = 0; v < 4; ++v) gp[(16 * ta + lg + 4 * v) * kp + 16 * tb + li] = acc[v];
+        }
+    }
 }
 
 // Threads per tensor of the factorisation (one workgroup per tensor).
 constexpr int kCholThreads = 256;
 
 template <int KT>
-__global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restrict__ gpart, double* __restrict__ xinv,
+__global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restrict__ gpart, double* __restrict__ lfac,
                                                   int* __restrict__ alive, int64_t gblocks, int k) {
     constexpr int kp = 16 * KT;
-    __shared__ double G[kp][kp + 1];  // Gram, then L in its lower triangle
-    __shared__ double X[kp][kp + 1];  // L^-1
-    __shared__ int dead[kp];
+    __shared__ double G[kp][kp + 1];  // Gram; its lower triangle is updated in place
+    __shared__ double L[kp][kp + 1];  // the factor, written column by column
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const double* gb = gpart + b * gblocks * kp * kp;
-    // G = sum of the block Grams in block order; blocks in the outer loop so that each
-    // thread's loads of one block are in flight together
+    // G = sum of the block Grams in block order.  The loads of kBlkBatch blocks are
+    // issued together (indices past the last block re-read it and are not added).
     constexpr int kEPT = (kp * kp + kCholThreads - 1) / kCholThreads;
+    constexpr int kBlkBatch = KT == 4 ? 4 : 8;
     double gs[kEPT];
+    for (int64_t q0 = 0; q0 < gblocks; q0 += kBlkBatch) {
+        double v[kBlkBatch][kEPT];
 #pragma unroll
-    for (int j = 0; j < kEPT; ++j) {
-        const int e = tid + kCholThreads * j;
-        gs[j] = e < kp * kp ? gb[e] : 0.0;
-    }
-    for (int64_t q = 1; q < gblocks; ++q) {
+        for (int qq = 0; qq < kBlkBatch; ++qq) {
+            const int64_t q = q0 + qq < gblocks ? q0 + qq : gblocks - 1;
 #pragma unroll
-        for (int j = 0; j < kEPT; ++j) {
-            const int e = tid + kCholThreads * j;
-            if (e < kp * kp) gs[j] += gb[q * kp * kp + e];
+            for (int j = 0; j < kEPT; ++j) {
+                const int e = tid + kCholThreads * j;
+                v[qq][j] = gb[q * kp * kp + (e < kp * kp ? e : 0)];
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < kBlkBatch; ++qq) {
+            if (q0 + qq >= gblocks) break;  // uniform; no memory operation below
+#pragma unroll
+            for (int j = 0; j < kEPT; ++j) gs[j] = q0 + qq == 0 ? v[qq][j] : gs[j] + v[qq][j];
         }
     }
 #pragma unroll
     for (int j = 0; j < kEPT; ++j) {
         const int e = tid + kCholThreads * j;
-        if (e < kp * kp) {
-            G[e / kp][e % kp] = gs[j];
-            X[e / kp][e % kp] = (e / kp == e % kp) ? 1.0 : 0.0;
-        }
+        if (e < kp * kp) G[e / kp][e % kp] = gs[j];
     }
     __syncthreads();
     double tr = 0.0;
     for (int j = 0; j < kp; ++j) tr += G[j][j];
     const double thresh = 1e-10 * tr;
     __syncthreads();  // every trace read precedes the in-place factorisation
+    // Right-looking Cholesky with one barrier per column.  Every thread reads the pivot
+    // d = G[j][j].  Column j of L goes to its own array, and the trailing lower
+    // triangle is updated from the unscaled column, G[i][l] -= G[i][j] G[l][j] / d for
+    // j < l <= i: the phase reads column j and writes only columns right of it.
+    // One reciprocal square root per column gives the pivot sqrt(d) = d / sqrt(d), the
+    // column scale 1 / sqrt(d) and 1 / d, which keeps the phase's dependent chain short.
+    static_assert(kp * kp % kCholThreads == 0, "the update covers whole rounds of the workgroup");
     for (int j = 0; j < kp; ++j) {
-        // every thread derives the pivot from the same LDS value, so no barrier is
-        // needed before the column is scaled; thread 0 alone writes it back
         const double d = G[j][j];
         const bool dj = !(j < k && d > thresh);
-        const double piv = dj ? 0.0 : sqrt(d);
-        for (int i = j + 1 + tid; i < kp; i += kCholThreads) G[i][j] = dj ? 0.0 : G[i][j] / piv;
-        __syncthreads();
-        if (tid == 0) {
-            G[j][j] = piv;
-            dead[j] = dj ? 1 : 0;
-        }
-        // trailing update of the lower triangle: G[i][l] -= L[i][j] L[l][j], j < l <= i
-        for (int e = tid; e < kp * kp; e += kCholThreads) {
+        const double rs = dj ? 0.0 : rsqrt(d);
+        const double inv_d = rs * rs;
+        for (int i = j + tid; i < kp; i += kCholThreads) L[i][j] = i == j ? d * rs : G[i][j] * rs;
+#pragma unroll
+        for (int q = 0; q < kp * kp / kCholThreads; ++q) {
+            const int e = tid + kCholThreads * q;
             const int i = e / kp, l = e % kp;
-            if (l > j && l <= i) G[i][l] -= G[i][j] * G[l][j];
+            if (l > j && l <= i) G[i][l] -= G[i][j] * G[l][j] * inv_d;
         }
         __syncthreads();
     }
-    // X = L^-1 by forward elimination on the rows of the identity
-    for (int j = 0; j < kp; ++j) {
-        const bool dj = dead[j] != 0;
-        for (int c = tid; c <= j; c += kCholThreads) X[j][c] = dj ? 0.0 : X[j][c] / G[j][j];
-        __syncthreads();
-        for (int e = tid; e < (kp - j - 1) * (j + 1); e += kCholThreads) {
-            const int i = j + 1 + e / (j + 1), c = e % (j + 1);
-            X[i][c] -= G[i][j] * X[j][c];
-        }
-        __syncthreads();
+    // Out: L below the diagonal, 1 / L[j][j] on it (0 for a dead column, whose pivot
+    // is 0), zeros above.
+    double* lb = lfac + b * kp * kp;
+    for (int e = tid; e < kp * kp; e += kCholThreads) {
+        const int j = e / kp, i = e % kp;
+        lb[e] = i < j ? L[j][i] : (i == j && L[j][j] > 0.0 ? 1.0 / L[j][j] : 0.0);
     }
-    double* xb = xinv + b * kp * kp;
-    for (int e = tid; e < kp * kp; e += kCholThreads) xb[e] = X[e / kp][e % kp];
-    if (tid < kp) alive[b * kp + tid] = dead[tid] ? 0 : 1;
+    if (tid < kp) alive[b * kp + tid] = L[tid][tid] > 0.0 ? 1 : 0;
 }
 
-// P[row][j] = sum_{i <= j} Y[row][i] X[j][i]; one row per thread, in place.
+// P[row] = Y[row] L^-T by forward substitution, p_j = (y_j - sum_{i<j} L[j][i] p_i) /
+// L[j][j], in fp64, one row per thread, in place over Y.  A dead column has 1/L[j][j]
+// = 0 and zeros below it in L, so its p_j is 0 and it feeds nothing later.  The factor
+// is staged in LDS by one cooperative load; every lane then reads the same address
+// (a broadcast).
 template <int KT>
-__global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const double* __restrict__ xinv,
+__global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const double* __restrict__ lfac,
                                                    int64_t m, int64_t batch) {
     constexpr int kp = 16 * KT;
-    __shared__ double X[kp][kp + 1];
+    __shared__ double lb[kp * kp];
     const int64_t rblocks = (m + 255) / 256;
     const int64_t b = blockIdx.x / rblocks;
     const int64_t row = (blockIdx.x % rblocks) * 256 + threadIdx.x;
-    const double* xb = xinv + b * kp * kp;
-    for (int e = threadIdx.x; e < kp * kp; e += 256) X[e / kp][e % kp] = xb[e];
+    for (int e = threadIdx.x; e < kp * kp; e += 256) lb[e] = lfac[b * kp * kp + e];
     __syncthreads();
     if (row >= m) return;
     float* pr = p + (b * m + row) * kp;
-    double y[kp];
+    double x[kp];
 #pragma unroll
     for (int i = 0; i < kp; i += 4) {
         const vf4 v = ld4(pr + i);
-        y[i] = v[0]; y[i + 1] = v[1]; y[i + 2] = v[2]; y[i + 3] = v[3];
+        x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
     }
 #pragma unroll
-    for (int j = 0; j < kp; j += 4) {
-        vf4 o;
+    for (int j = 0; j < kp; ++j) {
+        double acc = x[j];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            double acc = 0.0;
-#pragma unroll
-            for (int i = 0; i <= j + jj; ++i) acc = fma(y[i], X[j + jj][i], acc);
-            o[jj] = static_cast<float>(acc);
-        }
-        *reinterpret_cast<vf4*>(pr + j) = o;
+        for (int i = 0; i < j; ++i) acc = fma(-lb[j * kp + i], x[i], acc);
+        x[j] = acc * lb[j * kp + j];
     }
+#pragma unroll
+    for (int j = 0; j < kp; j += 4)
+        *reinterpret_cast<vf4*>(pr + j) = vf4{static_cast<float>(x[j]), static_cast<float>(x[j + 1]),
+                                              static_cast<float>(x[j + 2]), static_cast<float>(x[j + 3])};
 }
 
 // ---------------------------------------------------------- backproject ----
@@ -943,12 +962,12 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         int64_t gblocks = grid.gblocks;
         void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch};
         if ((e = go(&k_lr_gram<KT>, grid.gram, gargs, stream)) != hipSuccess) return e;
-        void* cargs[] = {(void*)&ws.gpart, (void*)&ws.xinv, (void*)&ws.alive, &gblocks, &k};
+        void* cargs[] = {(void*)&ws.gpart, (void*)&ws.lfac, (void*)&ws.alive, &gblocks, &k};
         if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>),
                                  dim3(static_cast<unsigned>(grid.chol)), dim3(kCholThreads), cargs, 0,
                                  stream)) != hipSuccess)
             return e;
-        void* sargs[] = {(void*)&ws.p, (void*)&ws.xinv, &m, &batch};
+        void* sargs[] = {(void*)&ws.p, (void*)&ws.lfac, &m, &batch};
         if ((e = go(&k_lr_solve<KT>, grid.solve, sargs, stream)) != hipSuccess) return e;
         void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal};
         if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
@@ -1016,7 +1035,7 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
         c += sz_al;
         ws.gpart = reinterpret_cast<double*>(c);
         c += sz_g;
-        ws.xinv = reinterpret_cast<double*>(c);
+        ws.lfac = reinterpret_cast<double*>(c);
         c += sz_x;
         ws.cmax = reinterpret_cast<float*>(c);
     }
