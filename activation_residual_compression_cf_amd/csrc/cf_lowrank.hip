@@ -518,48 +518,58 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 //              c = rint(x / s) clamped to [-7, 7] (0 if s = 0), nibbles packed low
 //              first along the rank index (or the fp32 factor copied); V's rows
 //              also refresh q_state where the column is alive.
-__device__ __forceinline__ float factor_elem(const float* x, int f, int64_t n, int kp, int64_t row, int kk) {
-    return f ? x[kk * n + row] : x[row * kp + kk];
+// The block's factor rows r0 .. r0 + nr - 1 into blk, rows past nr zero.  P rows are
+// kp consecutive floats, so the block is one contiguous span, read with coalesced
+// 16-byte loads; Q^T holds the factor transposed, so each rank index is a contiguous
+// run of the block's rows.  Either way every global access of a wave is one span.
+template <int kp>
+__device__ __forceinline__ void stage_factor_block(const float* x, int f, int64_t n, int64_t r0, int nr,
+                                                   float (*blk)[kp + 1]) {
+    const int t = threadIdx.x;
+    if (f) {
+#pragma unroll
+        for (int kk = 0; kk < kp; ++kk) blk[t][kk] = t < nr ? x[kk * n + r0 + t] : 0.0f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < kp / 4; ++i) {
+            const int e = 4 * (t + 256 * i);
+            const int r = e / kp, c = e % kp;
+            const vf4 v = r < nr ? ld4(x + r0 * kp + e) : vf4{0.f, 0.f, 0.f, 0.f};
+            blk[r][c] = v[0];
+            blk[r][c + 1] = v[1];
+            blk[r][c + 2] = v[2];
+            blk[r][c + 3] = v[3];
+        }
+    }
 }
 
 template <int KT>
 __global__ __launch_bounds__(256) void k_lr_colmax(const float* __restrict__ p, const float* __restrict__ qt,
                                                     float* __restrict__ cmax, int64_t m, int64_t n) {
     constexpr int kp = 16 * KT;
-    __shared__ float wmax[4][kp];
+    constexpr int TPC = 256 / kp;  // threads per column
+    __shared__ float blk[256][kp + 1];
+    __shared__ float part[kp][TPC + 1];
     const int64_t mb = (m + 255) / 256, nb = (n + 255) / 256;
     const int64_t b = blockIdx.x / (mb + nb);
-    const int64_t blk = blockIdx.x % (mb + nb);
-    const int f = blk >= mb;
-    const int64_t row = (f ? blk - mb : blk) * 256 + threadIdx.x;
+    const int64_t bi = blockIdx.x % (mb + nb);
+    const int f = bi >= mb;
+    const int64_t r0 = (f ? bi - mb : bi) * 256;
     const int64_t rows = f ? n : m;
-    const float* x = f ? qt + b * kp * n : p + b * m * kp;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float v[kp];
-    if (row >= rows) {
-#pragma unroll
-        for (int kk = 0; kk < kp; ++kk) v[kk] = 0.0f;
-    } else if (f) {  // Q^T: element kk of this row is x[kk * n + row] (coalesced over threads)
-#pragma unroll
-        for (int kk = 0; kk < kp; ++kk) v[kk] = fabsf(x[kk * n + row]);
-    } else {  // P: the row is kp consecutive floats
-#pragma unroll
-        for (int i = 0; i < kp; i += 4) {
-            const vf4 t = ld4(x + row * kp + i);
-            v[i] = fabsf(t[0]); v[i + 1] = fabsf(t[1]); v[i + 2] = fabsf(t[2]); v[i + 3] = fabsf(t[3]);
-        }
-    }
-#pragma unroll
-    for (int kk = 0; kk < kp; ++kk) {
-        float mx = v[kk];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (lane == 0) wmax[wave][kk] = mx;
-    }
+    const int nr = static_cast<int>(rows - r0 < 256 ? rows - r0 : 256);
+    stage_factor_block<kp>(f ? qt + b * kp * n : p + b * m * kp, f, n, r0, nr, blk);
+    __syncthreads();
+    // thread t: column t % kp over rows t / kp, t / kp + TPC, ...  (max is exact, so
+    // the order does not matter)
+    const int kk = threadIdx.x % kp, slot = threadIdx.x / kp;
+    float mx = 0.0f;
+    for (int r = slot; r < 256; r += TPC) mx = fmaxf(mx, fabsf(blk[r][kk]));
+    part[kk][slot] = mx;
     __syncthreads();
     if (threadIdx.x < kp) {
-        const int kk = threadIdx.x;
-        cmax[blockIdx.x * kp + kk] = fmaxf(fmaxf(wmax[0][kk], wmax[1][kk]), fmaxf(wmax[2][kk], wmax[3][kk]));
+        float mm = part[threadIdx.x][0];
+        for (int q = 1; q < TPC; ++q) mm = fmaxf(mm, part[threadIdx.x][q]);
+        cmax[blockIdx.x * kp + threadIdx.x] = mm;
     }
 }
 
@@ -572,139 +582,125 @@ __global__ __launch_bounds__(256) void k_lr_pack(const float* __restrict__ p, co
                                                   float* __restrict__ v_scales) {
     constexpr int kp = 16 * KT;
     constexpr int TPC = 256 / kp;  // threads per column when reducing the block maxima
+    __shared__ float blk[256][kp + 1];
     __shared__ float sc[kp];
     __shared__ float part[kp][TPC];
+    __shared__ int sal[kp];
+    const int t = threadIdx.x;
     const int64_t mb = (m + 255) / 256, nb = (n + 255) / 256;
     const int64_t b = blockIdx.x / (mb + nb);
-    const int64_t blk = blockIdx.x % (mb + nb);
-    const int f = blk >= mb;
-    const int64_t fblk = f ? blk - mb : blk;
-    const int64_t row = fblk * 256 + threadIdx.x;
+    const int64_t bi = blockIdx.x % (mb + nb);
+    const int f = bi >= mb;
+    const int64_t fblk = f ? bi - mb : bi;
+    const int64_t r0 = fblk * 256;
     const int64_t rows = f ? n : m;
-    const float* x = f ? qt + b * kp * n : p + b * m * kp;
-    if (factor_bits == 4) {
-        if (threadIdx.x < kp * TPC) {
-            const int kk = threadIdx.x % kp, slot = threadIdx.x / kp;
-            const float* cm = cmax + (b * (mb + nb) + (f ? mb : 0)) * kp + kk;
-            float mm = 0.0f;
-            for (int64_t q = slot; q < (f ? nb : mb); q += TPC) mm = fmaxf(mm, cm[q * kp]);
-            part[kk][slot] = mm;
-        }
-        __syncthreads();
-        if (threadIdx.x < kp) {
-            const int kk = threadIdx.x;
-            float mm = part[kk][0];
-            for (int q = 1; q < TPC; ++q) mm = fmaxf(mm, part[kk][q]);
-            const float s = mm / 7.0f;
-            sc[kk] = s;
-            if (fblk == 0 && kk < k) (f ? v_scales : u_scales)[b * k + kk] = s;
-        }
-        __syncthreads();
-        if (row < rows) {
-            float xv[kp];
-            if (f) {
+    const int nr = static_cast<int>(rows - r0 < 256 ? rows - r0 : 256);
+    stage_factor_block<kp>(f ? qt + b * kp * n : p + b * m * kp, f, n, r0, nr, blk);
+    if (t < kp) sal[t] = alive[b * kp + t];
+    if (factor_bits == 4 && t < kp * TPC) {
+        const int kk = t % kp, slot = t / kp;
+        const float* cm = cmax + (b * (mb + nb) + (f ? mb : 0)) * kp + kk;
+        float mm = 0.0f;
+        for (int64_t q = slot; q < (f ? nb : mb); q += TPC) mm = fmaxf(mm, cm[q * kp]);
+        part[kk][slot] = mm;
+    }
+    __syncthreads();
+    if (factor_bits == 4 && t < kp) {
+        float mm = part[t][0];
+        for (int q = 1; q < TPC; ++q) mm = fmaxf(mm, part[t][q]);
+        const float s = mm / 7.0f;
+        sc[t] = s;
+        if (fblk == 0 && t < k) (f ? v_scales : u_scales)[b * k + t] = s;
+    }
+    __syncthreads();
+    const int64_t row = r0 + t;
+    if (factor_bits == 4 && t < nr) {
+        uint32_t words[kp / 8];
 #pragma unroll
-                for (int kk = 0; kk < kp; ++kk) xv[kk] = x[kk * n + row];
-            } else {
+        for (int w = 0; w < kp / 8; ++w) words[w] = 0;
 #pragma unroll
-                for (int i = 0; i < kp; i += 4) {
-                    const vf4 t = ld4(x + row * kp + i);
-                    xv[i] = t[0]; xv[i + 1] = t[1]; xv[i + 2] = t[2]; xv[i + 3] = t[3];
-                }
+        for (int kk = 0; kk < kp; ++kk) {
+            const float s = sc[kk];
+            int c = 0;
+            if (kk < k && s > 0.0f) {
+                float q = rintf(blk[t][kk] / s);
+                q = fminf(fmaxf(q, -7.0f), 7.0f);
+                c = static_cast<int>(q);
             }
-            uint32_t words[kp / 8];
-#pragma unroll
-            for (int w = 0; w < kp / 8; ++w) words[w] = 0;
-#pragma unroll
-            for (int kk = 0; kk < kp; ++kk) {
-                const float s = sc[kk];
-                int c = 0;
-                if (kk < k && s > 0.0f) {
-                    float q = rintf(xv[kk] / s);
-                    q = fminf(fmaxf(q, -7.0f), 7.0f);
-                    c = static_cast<int>(q);
-                }
-                words[kk / 8] |= (static_cast<uint32_t>(c) & 0xFu) << (4 * (kk % 8));
-            }
-            // the row's k/2 bytes start at a 16-byte boundary when k % 32 == 0 (one
-            // 16-byte store per 32 codes), at a 4-byte boundary when k % 8 == 0
-            uint8_t* out = static_cast<uint8_t*>(f ? v : u) + (b * rows + row) * k / 2;
-            if ((k & 31) == 0 && (reinterpret_cast<uintptr_t>(u) & 15) == 0 &&
-                (reinterpret_cast<uintptr_t>(v) & 15) == 0) {
-#pragma unroll
-                for (int w = 0; w < kp / 8; w += 4)
-                    if (8 * w < k)
-                        *reinterpret_cast<uint4*>(out + 4 * w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
-            } else if ((k & 7) == 0) {
-#pragma unroll
-                for (int w = 0; w < kp / 8; ++w)
-                    if (8 * w < k) reinterpret_cast<uint32_t*>(out)[w] = words[w];
-            } else {
-                for (int q = 0; q < k / 2; ++q) out[q] = static_cast<uint8_t>(words[q / 4] >> (8 * (q % 4)));
-            }
+            words[kk / 8] |= (static_cast<uint32_t>(c) & 0xFu) << (4 * (kk % 8));
         }
-    } else if (factor_bits == 16 && row < rows) {
+        // the row's k/2 bytes start at a 16-byte boundary when k % 32 == 0 (one
+        // 16-byte store per 32 codes), at a 4-byte boundary when k % 8 == 0
+        uint8_t* out = static_cast<uint8_t*>(f ? v : u) + (b * rows + row) * k / 2;
+        if ((k & 31) == 0 && (reinterpret_cast<uintptr_t>(u) & 15) == 0 &&
+            (reinterpret_cast<uintptr_t>(v) & 15) == 0) {
+#pragma unroll
+            for (int w = 0; w < kp / 8; w += 4)
+                if (8 * w < k)
+                    *reinterpret_cast<uint4*>(out + 4 * w) = make_uint4(words[w], words[w + 1], words[w + 2], words[w + 3]);
+        } else if ((k & 7) == 0) {
+#pragma unroll
+            for (int w = 0; w < kp / 8; ++w)
+                if (8 * w < k) reinterpret_cast<uint32_t*>(out)[w] = words[w];
+        } else {
+            for (int q = 0; q < k / 2; ++q) out[q] = static_cast<uint8_t>(words[q / 4] >> (8 * (q % 4)));
+        }
+    } else if (factor_bits == 16 && t < nr) {
         // round-to-nearest-even bf16 of each element; 8-byte stores when k % 4 == 0
         uint16_t* out = static_cast<uint16_t*>(f ? v : u) + (b * rows + row) * k;
-        auto rne = [](float xf) -> uint32_t {
-            const uint32_t w = __float_as_uint(xf);
-            return (w + 0x7FFFu + ((w >> 16) & 1u)) >> 16;
-        };
         if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(f ? v : u) & 7) == 0) {
 #pragma unroll
             for (int kk = 0; kk < kp; kk += 4) {
                 if (kk >= k) break;
-                const uint32_t lo = rne(factor_elem(x, f, n, kp, row, kk)) |
-                                    (rne(factor_elem(x, f, n, kp, row, kk + 1)) << 16);
-                const uint32_t hi = rne(factor_elem(x, f, n, kp, row, kk + 2)) |
-                                    (rne(factor_elem(x, f, n, kp, row, kk + 3)) << 16);
+                const uint32_t lo = bf16_rne(blk[t][kk]) | (bf16_rne(blk[t][kk + 1]) << 16);
+                const uint32_t hi = bf16_rne(blk[t][kk + 2]) | (bf16_rne(blk[t][kk + 3]) << 16);
                 *reinterpret_cast<uint2*>(out + kk) = make_uint2(lo, hi);
             }
         } else {
-            for (int kk = 0; kk < k; ++kk) out[kk] = static_cast<uint16_t>(rne(factor_elem(x, f, n, kp, row, kk)));
+            for (int kk = 0; kk < k; ++kk) out[kk] = static_cast<uint16_t>(bf16_rne(blk[t][kk]));
         }
-    } else if (row < rows) {
+    } else if (factor_bits == 32 && t < nr) {
         float* out = static_cast<float*>(f ? v : u) + (b * rows + row) * k;
         if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(f ? v : u) & 15) == 0) {
 #pragma unroll
             for (int kk = 0; kk < kp; kk += 4) {
                 if (kk >= k) break;
-                *reinterpret_cast<vf4*>(out + kk) =
-                    vf4{factor_elem(x, f, n, kp, row, kk), factor_elem(x, f, n, kp, row, kk + 1),
-                        factor_elem(x, f, n, kp, row, kk + 2), factor_elem(x, f, n, kp, row, kk + 3)};
+                *reinterpret_cast<vf4*>(out + kk) = vf4{blk[t][kk], blk[t][kk + 1], blk[t][kk + 2], blk[t][kk + 3]};
             }
         } else {
-            for (int kk = 0; kk < k; ++kk) out[kk] = factor_elem(x, f, n, kp, row, kk);
+            for (int kk = 0; kk < k; ++kk) out[kk] = blk[t][kk];
         }
     }
-    if (f && row < rows) {
-        // q_state row = Q row where the column is alive, else its previous value;
-        // whole-row 16-byte stores when the layout allows (k % 4 == 0, aligned base)
-        float* qs = q_state + (b * n + row) * k;
-        const int* al = alive + b * kp;
+    if (f) {
+        // q_state rows r0 .. r0 + nr - 1 (one contiguous span of nr * k floats) = Q where
+        // the column is alive, else their previous value; written by the whole
+        // workgroup in 16-byte pieces when the layout allows (k % 4 == 0, aligned base)
+        float* qs = q_state + (b * n + r0) * k;
+        const int cnt = nr * k;
         if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(q_state) & 15) == 0) {
-#pragma unroll
-            for (int kk = 0; kk < kp; kk += 4) {
-                if (kk >= k) break;
-                vf4 o = vf4{x[kk * n + row], x[(kk + 1) * n + row], x[(kk + 2) * n + row], x[(kk + 3) * n + row]};
-                if (!(al[kk] && al[kk + 1] && al[kk + 2] && al[kk + 3])) {
-                    const vf4 old = ld4(qs + kk);
+            for (int e = 4 * t; e < cnt; e += 1024) {
+                const int r = e / k, c = e % k;
+                vf4 o = vf4{blk[r][c], blk[r][c + 1], blk[r][c + 2], blk[r][c + 3]};
+                if (!(sal[c] && sal[c + 1] && sal[c + 2] && sal[c + 3])) {
+                    const vf4 old = ld4(qs + e);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (!al[kk + j]) o[j] = old[j];
+                        if (!sal[c + j]) o[j] = old[j];
                 }
-                *reinterpret_cast<vf4*>(qs + kk) = o;
+                *reinterpret_cast<vf4*>(qs + e) = o;
             }
         } else {
-            for (int kk = 0; kk < k; ++kk)
-                if (al[kk]) qs[kk] = x[kk * n + row];
+            for (int e = t; e < cnt; e += 256) {
+                const int r = e / k, c = e % k;
+                if (sal[c]) qs[e] = blk[r][c];
+            }
         }
     }
 }
 
 // --------------------------------------------------------- reconstruct ----
-// Workgroup: 4 waves over columns [c0, c0 + 256) and rows [r0, r0 + 64), in 4
-// stages of 16 rows.  Wave w owns columns c0 + 64 w .. + 63 (4 MFMA tiles) and keeps
+// Workgroup: 4 waves over columns [c0, c0 + kRecCols) and rows [r0, r0 + kRecRows),
+// in stages of 16 rows.  Wave w owns columns c0 + 64 w .. + 63 (4 MFMA tiles) and keeps
 // their V^ operands in registers.  Per stage the MFMAs give
 // C'[i][j] = sum_kk V^[col i][kk] U^[row j][kk] = R^[row j][col i]  (lane l holds
 // R^[row0 + li][col + 4 lg .. + 3]); the 16 x 256 tile goes to LDS, then every wave
