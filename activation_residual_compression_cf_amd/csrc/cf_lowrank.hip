@@ -88,14 +88,40 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t total) {
 }
 
 // ---------------------------------------------------------------- prep ----
+// q_state (n x k per tensor, row-major) -> Q^T (kp x n, rank padded with zero rows).
+// Workgroup: 256 consecutive rows of one tensor's q_state, one contiguous span read
+// with coalesced loads into LDS, then written out one rank index at a time (256
+// consecutive floats of Q^T each).
+template <int KT>
 __global__ __launch_bounds__(256) void k_lr_prep(const float* __restrict__ q_state, float* __restrict__ qt,
-                                                  int64_t n, int k, int kp, int64_t batch) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // over batch*kp*n
-    if (idx >= batch * kp * n) return;
-    const int64_t c = idx % n;
-    const int kk = static_cast<int>((idx / n) % kp);
-    const int64_t b = idx / (n * kp);
-    qt[idx] = kk < k ? q_state[(b * n + c) * k + kk] : 0.0f;
+                                                  int64_t n, int k, int64_t batch) {
+    constexpr int kp = 16 * KT;
+    __shared__ float tile[256][kp + 1];
+    const int t = threadIdx.x;
+    const int64_t nb = (n + 255) / 256;
+    const int64_t b = blockIdx.x / nb;
+    const int64_t c0 = (blockIdx.x % nb) * 256;
+    const int nc = static_cast<int>(n - c0 < 256 ? n - c0 : 256);
+    const float* src = q_state + (b * n + c0) * k;  // nc rows of k floats
+    const int cnt = nc * k;
+    if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(q_state) & 15) == 0) {
+        for (int e = 4 * t; e < cnt; e += 1024) {
+            const vf4 v = ld4(src + e);
+            const int r = e / k, c = e % k;
+            tile[r][c] = v[0];
+            tile[r][c + 1] = v[1];
+            tile[r][c + 2] = v[2];
+            tile[r][c + 3] = v[3];
+        }
+    } else {
+        for (int e = t; e < cnt; e += 256) tile[e / k][e % k] = src[e];
+    }
+    __syncthreads();
+    if (t < nc) {
+        float* dst = qt + b * kp * n + c0 + t;
+#pragma unroll
+        for (int kk = 0; kk < kp; ++kk) dst[kk * n] = kk < k ? tile[t][kk] : 0.0f;
+    }
 }
 
 // ------------------------------------------------------------- project ----
@@ -901,7 +927,7 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
     g.kp = (rank + 15) / 16 * 16;
     g.nseg = (n + kSegCols - 1) / kSegCols;
     g.gblocks = (m + gram_rows(g.kp / 16) - 1) / gram_rows(g.kp / 16);
-    g.prep = (batch * g.kp * n + 255) / 256;
+    g.prep = batch * ((n + 255) / 256);
     g.project = round8(batch * ((m + kProjRows - 1) / kProjRows) * g.nseg);
     g.gram = batch * g.gblocks;
     g.chol = batch;
@@ -941,12 +967,11 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
                        int factor_bits, int64_t batch, float* q_state, void* u, float* u_scales, void* v,
                        float* v_scales, const LowrankWorkspace& ws, hipStream_t stream) {
     const LowrankGrids grid = lowrank_grids(m, n, k, batch);
-    int kp = 16 * KT;
     int64_t nseg = grid.nseg;
     hipError_t e;
     {
-        void* args[] = {&q_state, (void*)&ws.qt, &n, &k, &kp, &batch};
-        if ((e = go(&k_lr_prep, grid.prep, args, stream)) != hipSuccess) return e;
+        void* args[] = {&q_state, (void*)&ws.qt, &n, &k, &batch};
+        if ((e = go(&k_lr_prep<KT>, grid.prep, args, stream)) != hipSuccess) return e;
     }
     int64_t ptotal = grid.project;
     int64_t btotal = grid.backproject;

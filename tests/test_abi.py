@@ -129,9 +129,11 @@ def test_lowrank_validation(L):
     assert L.cf_lowrank_workspace_bytes(1024, 3072, 65, 1) == 0   # rank above 64
     assert L.cf_lowrank_workspace_bytes(32, 64, 48, 1) == 0       # rank above min(m, n)
     assert L.cf_lowrank_workspace_bytes(1024, 3072, 32, 2731) == 0  # batch*m*n above 2^33
-    # 16 x 2^28: the start-basis transpose would need 2^32 work-items in one dispatch
-    assert L.cf_lowrank_workspace_bytes(16, 1 << 28, 16, 1) == 0
-    assert L.cf_lowrank_workspace_bytes(16, 1 << 27, 16, 1) > 0
+    # 2^23 tensors of 16 x 16: the factor quantization would need 2^32 work-items in
+    # one dispatch (two 256-thread workgroups per tensor)
+    assert L.cf_lowrank_workspace_bytes(16, 16, 16, 1 << 23) == 0
+    assert L.cf_lowrank_workspace_bytes(16, 16, 16, 1 << 22) > 0
+    assert L.cf_lowrank_workspace_bytes(16, 1 << 28, 16, 1) > 0
     L.cf_lowrank_compress.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 3 +
                                       [ctypes.c_int64] * 2 + [ctypes.c_int] * 4 +
                                       [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p])
