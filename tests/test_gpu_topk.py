@@ -220,7 +220,8 @@ def test_failed_call_writes_nothing(cf, dev):
 
 def test_index_beyond_2_31_elements(cf, dev, O):
     """One call over 2^31 + 2^20 elements (64-bit indexing, group index * k beyond 2^32 at
-    k = 128); sampled groups at the start, around 2^31 and at the end."""
+    k = 128); sampled groups at the start, around 2^31 and at the end, and a receiver
+    decoding the same payload matches the sender on every element."""
     wl = gen.Workload("big", 1024, 3072, 1, 2, "bf16", True)
     tr = gen.Trajectory(wl, 5)
     t0, t1 = tr.next()[0].reshape(-1), tr.next()[0].reshape(-1)
@@ -234,10 +235,15 @@ def test_index_beyond_2_31_elements(cf, dev, O):
     ah = torch.empty(numel, dtype=torch.float32, device=dev)
     er = torch.empty(numel, dtype=torch.float32, device=dev)
     cf.init_state(a0_d, ah, er)
+    rx = torch.empty(numel, dtype=torch.float32, device=dev)
+    cf.init_state(a0_d, rx)
     del a0_d
     a1_d = to_dev(a1, dev)
     idx, vals = cf.topk_compress(k, a1_d, ah, er)
+    cf.topk_decompress(k, idx, vals, rx)
     torch.cuda.synchronize()
+    assert torch.equal(rx, ah), "receiver != sender beyond 2^31 elements"
+    del rx
     ng = numel // 128
     for g0 in (0, (1 << 31) // 128 - 8, ng - 64):
         sl = slice(g0 * 128, (g0 + 64) * 128)
