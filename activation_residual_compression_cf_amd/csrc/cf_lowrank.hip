@@ -798,30 +798,99 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     const int64_t nrows = r0 + kRecRows < m ? kRecRows : m - r0;  // multiple of 16
     const int nst = static_cast<int>(nrows / kStage);
 
-    // U^ rows of this workgroup (2 KS values per thread) and the V^ operands of this
-    // wave's 4 column tiles (k-slice s: V^[col][4 s + lg]), each a batch of loads issued
-    // together; rows and columns past the tensor are clamped and read as 0.
+    // U^ rows of this workgroup (KS / 2 values per thread, into uh) and the V^ operands
+    // of this wave's 4 column tiles (k-slice s: V^[col][4 s + lg]); rows and columns past
+    // the tensor read as 0.
     constexpr int kUPT = kRecRows * 4 * KS / 256;
-    float uvals[kUPT];
-#pragma unroll
-    for (int j = 0; j < kUPT; ++j) {
-        const int e = threadIdx.x + 256 * j;
-        const int rr = e / (4 * KS), kk = e % (4 * KS);
-        uvals[j] = factor_sel<FB>(ub, usb, r0 + (rr < nrows ? rr : nrows - 1), k, kk, rr < nrows);
-    }
     const int64_t wc0 = c0 + 64 * wave;
     float av[4][KS];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int64_t col = wc0 + 16 * it + li;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) av[it][s] = factor_sel<FB>(vb, vsb, col < n ? col : n - 1, k, 4 * s + lg, col < n);
-    }
-#pragma unroll
-    for (int j = 0; j < kUPT; ++j) {
-        const int e = threadIdx.x + 256 * j;
-        uh[e / (4 * KS)][e % (4 * KS)] = uvals[j];
-    }
+    auto setup_operands = [&]() {
+        if constexpr (FB == 4) {
+            // INT4: the workgroup's code bytes (its 256 columns of V, its 32 rows of U; each
+            // a contiguous, 4-byte aligned span) and both scale vectors are staged in LDS by
+            // a few dword loads per thread, and the nibbles are taken from there.  Per-lane
+            // byte loads of the operands would outnumber the streaming loads several times.
+            constexpr int kVW = kRecCols * 4 * KS / 8;  // dwords of V codes for 4 KS >= k
+            constexpr int kUW = kRecRows * 4 * KS / 8;
+            __shared__ uint32_t vcode[kVW];
+            __shared__ uint32_t ucode[kUW];
+            __shared__ float vsc[4 * KS], usc[4 * KS];
+            const int64_t ncols = c0 + kRecCols <= n ? kRecCols : n - c0;  // multiple of 16
+            const int vwords = static_cast<int>(ncols * k / 8), uwords = static_cast<int>(nrows * k / 8);
+            const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(vb) + c0 * k / 2);
+            const uint32_t* usrc = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(ub) + r0 * k / 2);
+            uint32_t vw[(kVW + 255) / 256], uw[(kUW + 255) / 256];
+    #pragma unroll
+            for (int j = 0; j < (kVW + 255) / 256; ++j) {
+                const int e = threadIdx.x + 256 * j;
+                vw[j] = vsrc[e < vwords ? e : vwords - 1];
+            }
+    #pragma unroll
+            for (int j = 0; j < (kUW + 255) / 256; ++j) {
+                const int e = threadIdx.x + 256 * j;
+                uw[j] = usrc[e < uwords ? e : uwords - 1];
+            }
+            const int ks = threadIdx.x < 4 * KS ? threadIdx.x : 0;
+            const float vs_ = vsb[ks < k ? ks : k - 1], us_ = usb[ks < k ? ks : k - 1];
+    #pragma unroll
+            for (int j = 0; j < (kVW + 255) / 256; ++j)
+                if (threadIdx.x + 256 * j < kVW) vcode[threadIdx.x + 256 * j] = vw[j];
+    #pragma unroll
+            for (int j = 0; j < (kUW + 255) / 256; ++j)
+                if (threadIdx.x + 256 * j < kUW) ucode[threadIdx.x + 256 * j] = uw[j];
+            if (threadIdx.x < 4 * KS) {
+                vsc[threadIdx.x] = threadIdx.x < k ? vs_ : 0.0f;
+                usc[threadIdx.x] = threadIdx.x < k ? us_ : 0.0f;
+            }
+            __syncthreads();
+            const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(vcode);
+            const uint8_t* ubytes = reinterpret_cast<const uint8_t*>(ucode);
+            auto nib = [](uint8_t byte, int kk) {
+                const int c = (kk & 1) ? (byte >> 4) : (byte & 0xF);
+                return static_cast<float>(c >= 8 ? c - 16 : c);
+            };
+    #pragma unroll
+            for (int j = 0; j < kUPT; ++j) {
+                const int e = threadIdx.x + 256 * j;
+                const int rr = e / (4 * KS), kk = e % (4 * KS);
+                const bool keep = rr < nrows && kk < k;
+                const float x = nib(ubytes[(keep ? rr * k + kk : 0) >> 1], kk) * usc[kk];
+                uh[rr][kk] = keep ? x : 0.0f;
+            }
+    #pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int cc = 64 * wave + 16 * it + li;  // column within the workgroup
+    #pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int kk = 4 * s + lg;
+                    const bool keep = cc < ncols && kk < k;
+                    const float x = nib(vbytes[(keep ? cc * k + kk : 0) >> 1], kk) * vsc[kk];
+                    av[it][s] = keep ? x : 0.0f;
+                }
+            }
+        } else {
+            // 16-bit and fp32 factors: batches of per-lane loads issued together.
+            float uvals[kUPT];
+    #pragma unroll
+            for (int j = 0; j < kUPT; ++j) {
+                const int e = threadIdx.x + 256 * j;
+                const int rr = e / (4 * KS), kk = e % (4 * KS);
+                uvals[j] = factor_sel<FB>(ub, usb, r0 + (rr < nrows ? rr : nrows - 1), k, kk, rr < nrows);
+            }
+    #pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int64_t col = wc0 + 16 * it + li;
+    #pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    av[it][s] = factor_sel<FB>(vb, vsb, col < n ? col : n - 1, k, 4 * s + lg, col < n);
+            }
+    #pragma unroll
+            for (int j = 0; j < kUPT; ++j) {
+                const int e = threadIdx.x + 256 * j;
+                uh[e / (4 * KS)][e % (4 * KS)] = uvals[j];
+            }
+        }
+    };
 
     const int64_t mn = m * n;
     const int64_t col = c0 + 4 * lane;  // streaming column of this lane
@@ -853,7 +922,8 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
         };
         fill(hb[0], xb[0], 0);
         fill(hb[1], xb[1], 1);
-        __syncthreads();  // uh is complete
+        setup_operands();  // its factor loads overlap the streaming loads above
+        __syncthreads();   // uh is complete
 #pragma unroll
         for (int st = 0; st < kNS; ++st) {
 #pragma unroll
@@ -877,6 +947,7 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
         }
         return;
     }
+    setup_operands();
     load_stage(0);
     __syncthreads();  // uh is complete
     for (int st = 0; st < nst; ++st) {
