@@ -91,6 +91,17 @@ def _need(name: str, t: torch.Tensor | None, nbytes: int, valid: bool = True):
         raise ValueError(f"{name} holds {t.numel() * t.element_size()} B, the call needs {nbytes} B")
 
 
+_F32, _U8 = torch.float32, torch.uint8
+_BITS16 = (torch.int16, torch.uint16, torch.bfloat16)  # raw 16-bit (bf16) storage
+
+
+def _dtype(name: str, t: torch.Tensor | None, *allowed):
+    """The C ABI takes untyped pointers: refuse a buffer whose element type the kernel
+    would misread (state and scales are fp32, codes and index bytes uint8)."""
+    if t is not None and t.dtype not in allowed:
+        raise TypeError(f"{name} is {t.dtype}; libcf wants {' or '.join(map(str, allowed))}")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -139,6 +150,8 @@ class SenderState:
 
 def init_state(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None = None, stream=None):
     """Warmup: ahat = a, err = 0 (err None on the receiver)."""
+    _dtype("ahat", ahat, _F32)
+    _dtype("err", err, _F32)
     _check("cf_init_state", lib.cf_init_state(_act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
                                               a.numel(), _stream(stream)))
 
@@ -152,6 +165,8 @@ def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor |
         codes = torch.empty(max(n * bits // 8, 0), dtype=torch.uint8, device=a.device)
     if scales is None:
         scales = torch.empty(max(n // GROUP, 0), dtype=torch.float32, device=a.device)
+    for nm, t, dt in (("ahat", ahat, _F32), ("err", err, _F32), ("codes", codes, _U8), ("scales", scales, _F32)):
+        _dtype(nm, t, dt)
     for nm, t, nb in (("ahat", ahat, 4 * n), ("err", err, 4 * n), ("codes", codes, n * bits // 8),
                       ("scales", scales, 4 * (n // GROUP))):
         _need(nm, t, nb, bits in (1, 2))
@@ -165,6 +180,8 @@ def decompress(bits: int, codes: torch.Tensor, scales: torch.Tensor, ahat: torch
     """Receiver step: ahat += decoded residual; with out_bf16 (a bfloat16 tensor of the
     same size) also writes the updated reconstruction rounded to bf16."""
     n = ahat.numel()
+    for nm, t, dt in (("codes", codes, _U8), ("scales", scales, _F32), ("ahat", ahat, _F32)):
+        _dtype(nm, t, dt)
     _need("codes", codes, n * bits // 8, bits in (1, 2))
     _need("scales", scales, 4 * (n // GROUP), bits in (1, 2))
     if out_bf16 is None:
@@ -186,6 +203,9 @@ def compress_ablation(mode: int, bits: int, a: torch.Tensor, ahat: torch.Tensor,
         codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=a.device)
     if scales is None:
         scales = torch.empty(n // GROUP, dtype=torch.float32, device=a.device)
+    for nm, t, dt in (("ahat", ahat, _F32), ("a_prev", a_prev, a.dtype), ("codes", codes, _U8),
+                      ("scales", scales, _F32)):
+        _dtype(nm, t, dt)
     for nm, t, nb in (("ahat", ahat, 4 * n), ("a_prev", a_prev, n * a.element_size()),
                       ("codes", codes, n * bits // 8), ("scales", scales, 4 * (n // GROUP))):
         _need(nm, t, nb, bits in (1, 2))
@@ -204,6 +224,8 @@ def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor
     if vals is None:
         vals = torch.empty(slots, dtype=torch.int16, device=a.device)
     n = a.numel()
+    for nm, t, dts in (("ahat", ahat, (_F32,)), ("err", err, (_F32,)), ("idx", idx, (_U8,)), ("vals", vals, _BITS16)):
+        _dtype(nm, t, *dts)
     for nm, t, nb in (("ahat", ahat, 4 * n), ("err", err, 4 * n), ("idx", idx, slots), ("vals", vals, 2 * slots)):
         _need(nm, t, nb, 1 <= k <= GROUP)
     _check("cf_topk_compress", lib.cf_topk_compress(k, _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
@@ -214,6 +236,9 @@ def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor
 def topk_decompress(k: int, idx: torch.Tensor, vals: torch.Tensor, ahat: torch.Tensor, stream=None):
     """Receiver step: ahat[group, idx] += bf16 value, for every sent slot."""
     slots = max(ahat.numel() // GROUP * k, 0)
+    _dtype("idx", idx, _U8)
+    _dtype("vals", vals, *_BITS16)
+    _dtype("ahat", ahat, _F32)
     _need("idx", idx, slots, 1 <= k <= GROUP)
     _need("vals", vals, 2 * slots, 1 <= k <= GROUP)
     _check("cf_topk_decompress", lib.cf_topk_decompress(k, _ptr(idx), _ptr(vals), _ptr(ahat), ahat.numel(),
@@ -292,6 +317,8 @@ class Slab:
 
     def decompress(self, codes: torch.Tensor, scales: torch.Tensor, per_call: int = 2, stream=None):
         s, bits, n = _stream(stream), self.bits, self.numel
+        _dtype("codes", codes, _U8)
+        _dtype("scales", scales, _F32)
         _need("codes", codes, self.count * n * bits // 8)
         _need("scales", scales, 4 * self.count * (n // GROUP))
         cb, sb, hb = _dev_ptr(codes), _dev_ptr(scales), _dev_ptr(self.ahat)
@@ -327,6 +354,11 @@ def _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload):
     esz = {4: 0.5, 16: 2, 32: 4}.get(factor_bits)
     if esz is None or rank < 1:
         return  # the C ABI rejects these arguments itself
+    fdt = {4: (_U8,), 16: _BITS16, 32: (_F32,)}[factor_bits]
+    _dtype("u", u, *fdt)
+    _dtype("v", v, *fdt)
+    _dtype("u_scales", us, _F32)
+    _dtype("v_scales", vs, _F32)
     _need("u", u, int(batch * m * rank * esz))
     _need("v", v, int(batch * n * rank * esz))
     if factor_bits == 4:
@@ -348,6 +380,8 @@ def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | No
         workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
     _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload)
     numel = batch * m * n
+    for nm, t in (("ahat", ahat), ("err", err), ("q_state", q_state)):
+        _dtype(nm, t, _F32)
     for nm, t, nb in (("ahat", ahat, 4 * numel), ("err", err, 4 * numel), ("q_state", q_state, 4 * batch * n * rank)):
         _need(nm, t, nb, rank >= 1)
     _check("cf_lowrank_compress", lib.cf_lowrank_compress(
@@ -361,6 +395,7 @@ def lowrank_decompress(factor_bits: int, payload, ahat: torch.Tensor, rank: int,
     """Receiver step on a (batch, m, n) reconstruction: ahat += U^ V^^T."""
     batch, m, n = ahat.shape
     u, us, v, vs = payload
+    _dtype("ahat", ahat, _F32)
     _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload)
     _check("cf_lowrank_decompress", lib.cf_lowrank_decompress(
         factor_bits, _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _ptr(ahat), m, n, rank, batch,

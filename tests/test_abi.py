@@ -249,6 +249,32 @@ def test_binding_refuses_host_tensors():
         cf.topk_compress(4, a, ah, er, torch.zeros(8, dtype=torch.uint8), torch.zeros(8, dtype=torch.int16))
 
 
+def test_binding_refuses_wrong_element_types():
+    """State and scales must be fp32, codes and index bytes uint8: the C ABI takes untyped
+    pointers, so the binding refuses other element types before any call."""
+    import torch
+
+    from activation_residual_compression_cf_amd import cf
+
+    a = torch.zeros(256, dtype=torch.bfloat16)
+    f32, f64 = torch.zeros(256), torch.zeros(256, dtype=torch.float64)
+    u8 = torch.zeros(32, dtype=torch.uint8)
+    with pytest.raises(TypeError, match="ahat"):
+        cf.compress(1, a, f64, f32, u8, torch.zeros(2))
+    with pytest.raises(TypeError, match="codes"):
+        cf.compress(1, a, f32, f32, torch.zeros(32, dtype=torch.int8), torch.zeros(2))
+    with pytest.raises(TypeError, match="scales"):
+        cf.decompress(1, u8, torch.zeros(2, dtype=torch.float16), f32)
+    with pytest.raises(TypeError, match="vals"):
+        cf.topk_compress(4, a, f32, f32, torch.zeros(8, dtype=torch.uint8), torch.zeros(8, dtype=torch.float32))
+    with pytest.raises(TypeError, match="q_state"):
+        cf.lowrank_compress(torch.zeros((1, 16, 16), dtype=torch.bfloat16), torch.zeros((1, 16, 16)), None,
+                            torch.zeros((1, 16, 2), dtype=torch.float64), 2, 1, 4,
+                            payload=(torch.zeros(16, dtype=torch.uint8), torch.zeros(2),
+                                     torch.zeros(16, dtype=torch.uint8), torch.zeros(2)),
+                            workspace=torch.zeros(1, dtype=torch.uint8))
+
+
 def test_error_buffer_is_optional_for_senders(L):
     """err = NULL is accepted by every sender (the error feedback lives in ahat); the
     valid calls stop at the device check."""
