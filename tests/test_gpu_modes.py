@@ -1,6 +1,7 @@
 """GPU parity of the ablation sender modes (cf_compress_ablation), the decode with a
 bf16 output (cf_decompress_bf16, several peers in one call), the error-feedback study
-on a whole trajectory, and checkpoint/resume of the sender state."""
+on a whole trajectory, checkpoint/resume of the sender state, and resynchronisation
+after a lost payload."""
 from __future__ import annotations
 
 import numpy as np
@@ -148,3 +149,29 @@ def test_checkpoint_resume(cf, dev):
     torch.cuda.synchronize()
     for x, y in ((s1.ahat, s2.ahat), (s1.err, s2.err), (s1.codes, s2.codes), (s1.scales, s2.scales)):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_resync_after_a_lost_payload(cf, dev, bits):
+    """A receiver that misses one step's payload drifts from the sender; the warmup run
+    again on both sides (the activation itself sent once) restores bit-identity, and the
+    later steps stay identical."""
+    wl = gen.Workload("resync", 256, 3072, 2, 8, "bf16", True)
+    tr = gen.Trajectory(wl, 11)
+    A = [to_dev(tr.next(), dev) for _ in range(8)]
+    say(f"resync after a lost payload, bits={bits}")
+    tx = cf.Slab(2, wl.numel, bits, dev)
+    rx = cf.Slab(2, wl.numel, bits, dev, receiver=True)
+    tx.init(A[0])
+    rx.init(A[0])
+    for t in range(1, 8):
+        if t == 5:
+            tx.init(A[t])
+            rx.init(A[t])
+        else:
+            tx.compress(A[t])
+            if t != 3:  # step 3's payload is lost
+                rx.decompress(tx.codes, tx.scales)
+        torch.cuda.synchronize()
+        same = torch.equal(rx.ahat, tx.ahat)
+        assert same == (t < 3 or t >= 5), f"step {t}: receiver {'equals' if same else 'differs from'} sender"
