@@ -226,7 +226,9 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
             const int rr = e / kp, kk = e % kp;
             yp[rr * kp + kk] = ((red[0][rr][kk] + red[1][rr][kk]) + red[2][rr][kk]) + red[3][rr][kk];
         }
-        __syncthreads();
+        // No barrier here: the next stage writes the slab, whose reads all ended before
+        // the barrier above, and writes red only after its first barrier, which every
+        // wave reaches after its own reads of red.
     }
 }
 
@@ -449,8 +451,8 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
                                                          int64_t batch, int64_t total) {
     constexpr int kp = 16 * KT;
     constexpr int kStage = 16;
-    __shared__ float slab[kStage][kBackCols + 4];
-    __shared__ float ps[kStage][kp + 1];
+    __shared__ float slab[2][kStage][kBackCols + 4];
+    __shared__ float ps[2][kStage][kp + 1];
     const int64_t cblocks = (n + kBackCols - 1) / kBackCols;
     const int64_t lw = xcd_remap(blockIdx.x, total);
     if (lw >= batch * cblocks) return;  // uniform per workgroup
@@ -472,12 +474,13 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
     // valid column whose products only reach output columns that are never stored.
     const int64_t col = c0 + 4 * lane < n ? c0 + 4 * lane : n - 4;
     const int64_t nst = m / kStage;
-    // Three stage buffers rotated by name (the loop is unrolled by three), two stages
-    // in flight while one is multiplied.  Every load is unconditional (stages past the
-    // end reload the last one and are never used), so the compiler waits for exactly
-    // the buffer a stage needs.
-    vf4 rq[3][4];
-    float pq[3][KT];
+    // Two register buffers and two LDS buffers, addressed by name (the loop is unrolled
+    // by two).  While a stage's MFMAs run on one LDS buffer, the wave waits for the next
+    // stage's loads and writes them into the other, so each stage needs one barrier and
+    // the multiply overlaps the wait.  Every load is unconditional (stages past the end
+    // reload the last one and are never used).
+    vf4 rq[2][4];
+    float pq[2][KT];
     auto fetch = [&](vf4 (&rx)[4], float (&px)[KT], int64_t st) {
         const int64_t sr = (st < nst ? st : nst - 1) * kStage;
 #pragma unroll
@@ -488,38 +491,45 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
             px[j] = pb[(sr + e / kp) * kp + e % kp];
         }
     };
-    auto stage = [&](vf4 (&rx)[4], float (&px)[KT], int64_t st) {
+    auto put = [&](float (&sl)[kStage][kBackCols + 4], float (&pp)[kStage][kp + 1], const vf4 (&rx)[4],
+                   const float (&px)[KT]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&slab[4 * wave + q][4 * lane]) = rx[q];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&sl[4 * wave + q][4 * lane]) = rx[q];
 #pragma unroll
         for (int j = 0; j < KT; ++j) {
             const int e = threadIdx.x + 256 * j;
-            ps[e / kp][e % kp] = px[j];
+            pp[e / kp][e % kp] = px[j];
         }
-        __syncthreads();
-        fetch(rx, px, st + 3);  // refill this buffer three stages ahead
+    };
+    auto mult = [&](float (&sl)[kStage][kBackCols + 4], float (&pp)[kStage][kp + 1]) {
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const vf4 rv = *reinterpret_cast<const vf4*>(&slab[4 * rg + lg][64 * wave + 4 * li]);
+            const vf4 rv = *reinterpret_cast<const vf4*>(&sl[4 * rg + lg][64 * wave + 4 * li]);
             float pv[KT];
 #pragma unroll
-            for (int t = 0; t < KT; ++t) pv[t] = ps[4 * rg + lg][16 * t + li];
+            for (int t = 0; t < KT; ++t) pv[t] = pp[4 * rg + lg][16 * t + li];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int t = 0; t < KT; ++t) acc[i][t] = mfma4(pv[t], rv[i], acc[i][t]);
         }
-        __syncthreads();
     };
     fetch(rq[0], pq[0], 0);
     fetch(rq[1], pq[1], 1);
-    fetch(rq[2], pq[2], 2);
-    for (int64_t st = 0; st < nst; st += 3) {
-        stage(rq[0], pq[0], st);
+    put(slab[0], ps[0], rq[0], pq[0]);
+    fetch(rq[0], pq[0], 2);
+    __syncthreads();
+    for (int64_t st = 0; st < nst; st += 2) {
+        // stage st is in LDS buffer 0, stage st + 1 in rq[1], stage st + 2 in rq[0]
+        mult(slab[0], ps[0]);
+        put(slab[1], ps[1], rq[1], pq[1]);
+        fetch(rq[1], pq[1], st + 3);
+        __syncthreads();
         if (st + 1 >= nst) break;
-        stage(rq[1], pq[1], st + 1);
-        if (st + 2 >= nst) break;
-        stage(rq[2], pq[2], st + 2);
+        mult(slab[1], ps[1]);
+        put(slab[0], ps[0], rq[0], pq[0]);
+        fetch(rq[0], pq[0], st + 4);
+        __syncthreads();
     }
     // acc[i][t] lane: Q^T row 16 t + 4 lg + v, column c0 + 64 w + 4 li + i
     float* qtb = qt + b * kp * n;
