@@ -20,9 +20,11 @@
 // reconstruction and error written once, codes and the scale written once per
 // group.  No atomics, no inter-block communication.
 //
-// Launch shape: large calls (a whole denoising step of many tensors) use one
-// instruction per stream per tile; the senders run one-wave blocks (measured 2-3%
-// faster on a FLUX step than 256-thread blocks).  Small calls (a single layer) use two instructions per tile and
+// Launch shape (measured on MI355X): the senders run one instruction per stream per
+// tile in one-wave blocks at every call size (2-3% faster than 256-thread blocks on a
+// whole FLUX step, 1.5% faster than two instructions per tile in 128-thread blocks on
+// one layer's K and V).  The decode of a whole step runs 256-thread blocks, its bf16
+// variant one-wave blocks; a small decode call uses two instructions per tile and
 // 128-thread blocks, which keeps more bytes in flight per wave when the grid alone
 // cannot fill the chip for long.
 //
@@ -211,16 +213,17 @@ __global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict_
 }
 
 // Warmup: ahat = a (widened), err = 0 when err is given.  4 elements per thread.
-template <typename ActT>
-__global__ __launch_bounds__(256) void k_init(const ActT* __restrict__ a, float* __restrict__ ahat,
-                                               float* __restrict__ err, int64_t nquads) {
-    const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+template <typename ActT, int BLOCK = 256>
+__global__ __launch_bounds__(BLOCK) void k_init(const ActT* __restrict__ a, float* __restrict__ ahat,
+                                                 float* __restrict__ err, int64_t nquads) {
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * BLOCK + threadIdx.x;
     if (q >= nquads) return;
     st_nt(ahat + q * 4, load_act4(a, q * 4));
     if (err) st_nt(err + q * 4, vf4{0.f, 0.f, 0.f, 0.f});
 }
 
-// Calls of at least this many groups (about 8 FLUX-shard tensors) take the large shape.
+// Decode calls of at least this many groups (about 8 FLUX-shard tensors) take the large
+// shape.
 constexpr int64_t kLargeCall = int64_t(1) << 17;
 
 template <typename K>
@@ -236,9 +239,7 @@ template <int BITS, typename ActT, int MODE>
 hipError_t run_compress(const ActT* a, const ActT* a_prev, float* ahat, float* err, uint8_t* codes,
                         float* scales, int64_t ngroups, hipStream_t stream) {
     void* args[] = {&a, &a_prev, &ahat, &err, &codes, &scales, &ngroups};
-    if (ngroups >= kLargeCall)
-        return launch(&k_compress<BITS, ActT, 1, 64, MODE>, ngroups, 1, 64, args, stream);
-    return launch(&k_compress<BITS, ActT, 2, 128, MODE>, ngroups, 2, 128, args, stream);
+    return launch(&k_compress<BITS, ActT, 1, 64, MODE>, ngroups, 1, 64, args, stream);
 }
 
 template <typename ActT, int MODE>

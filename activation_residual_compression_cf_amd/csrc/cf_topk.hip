@@ -147,12 +147,12 @@ __device__ __forceinline__ void topk_group(RawT raw, vf2 h, int64_t g, int lane,
     pay.put(slot1, sel1, lane * 2 + 1, v1);
 }
 
-template <typename ActT, bool STAGED, bool HAS_E>
-__global__ __launch_bounds__(kBlock) void k_topk_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
+template <typename ActT, bool STAGED, bool HAS_E, int BLOCK = kBlock>
+__global__ __launch_bounds__(BLOCK) void k_topk_compress(const ActT* __restrict__ a, float* __restrict__ ahat,
                                                           float* __restrict__ err, uint8_t* __restrict__ idx,
                                                           uint16_t* __restrict__ vals, int k, int64_t ngroups) {
     using RawT = decltype(load_pair(a, 0));
-    constexpr int kWaves = kBlock / 64;
+    constexpr int kWaves = BLOCK / 64;
     __shared__ uint32_t sidx[STAGED ? kWaves : 1][kPerWave * kGroup / 4];
     __shared__ uint32_t sval[STAGED ? kWaves : 1][kPerWave * kGroup / 2];
     const int lane = threadIdx.x & 63;
@@ -215,10 +215,11 @@ __global__ __launch_bounds__(kBlock) void k_topk_compress(const ActT* __restrict
 // in the wave so that the table never needs clearing; each lane then reads its two
 // elements' words and adds the value where the tag matches.  Scattered 4-byte updates
 // would touch most 64-byte sectors of a group anyway and leave them partly written.
-__global__ __launch_bounds__(kBlock) void k_topk_decompress(const uint8_t* __restrict__ idx,
+template <int BLOCK = kBlock>
+__global__ __launch_bounds__(BLOCK) void k_topk_decompress(const uint8_t* __restrict__ idx,
                                                             const uint16_t* __restrict__ vals,
                                                             float* __restrict__ ahat, int k, int64_t ngroups) {
-    constexpr int kWaves = kBlock / 64;
+    constexpr int kWaves = BLOCK / 64;
     __shared__ uint32_t table[kWaves][kGroup];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -296,7 +297,7 @@ hipError_t launch_topk_decompress(int k, const uint8_t* idx, const uint16_t* val
     void* args[] = {&idx, &vals, &ahat, &k, &ng};
     const int64_t waves = (ng + kPerWave - 1) / kPerWave;
     const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&k_topk_decompress), dim3(static_cast<unsigned>(blocks)),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_topk_decompress<kBlock>), dim3(static_cast<unsigned>(blocks)),
                            dim3(kBlock), args, 0, stream);
 }
 

@@ -268,7 +268,7 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": "k_compress<1, bf16> (one wave instruction per stream per 2-group tile, 256 threads)" if per_call * numel // 128 >= (1 << 17) else "k_compress<1, bf16> (two instructions per stream per 4-group tile, 128 threads)",
+        "kernel": "k_compress<1, bf16> (one wave instruction per stream per 2-group tile, one-wave blocks)",
         "algorithmic_bytes_per_launch": int(algo_bytes),
         "avg_launch_us": round(avg_launch_ms * 1e3, 2),
         "launches_timed": n_launch,
