@@ -791,7 +791,10 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     __shared__ float uh[kRecRows][4 * KS + 1];  // dequantized U^ rows of this workgroup
     const int64_t rblocks = (m + kRecRows - 1) / kRecRows;
     const int64_t cblocks = (n + kRecCols - 1) / kRecCols;
-    const int64_t lw = xcd_remap(blockIdx.x, total);
+    // Tiles in hardware order: unlike the projections, whose many workgroups per tensor
+    // re-read the same small operands, the reconstruction streams faster when
+    // consecutive tiles go to different XCDs (measured 3% over per-XCD ranges).
+    const int64_t lw = static_cast<int64_t>(blockIdx.x);
     if (lw >= batch * rblocks * cblocks) return;  // uniform per workgroup
     const int64_t b = lw / (rblocks * cblocks);
     const int64_t r0 = ((lw / cblocks) % rblocks) * kRecRows;
