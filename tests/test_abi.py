@@ -1,7 +1,9 @@
 """The C ABI library: it loads, exports every symbol the headers declare, and its
 validation (which runs before any HIP call) rejects bad arguments.  No compute call
 is made here: pointers are fake addresses that are never dereferenced, and a fully
-valid call stops at the device check where there is no gfx950."""
+valid call stops at the device check where there is no gfx950.  On a machine with a
+GPU driver those valid calls would be launched, so the validation tests are skipped
+there (the GPU tests cover the same entry points with real buffers)."""
 import ctypes
 import glob
 import os
@@ -25,10 +27,18 @@ def declared_symbols():
 
 
 @pytest.fixture(scope="module")
-def L():
+def lib():
+    """The library, for calls that never reach the device check."""
     if not os.path.exists(LIB):
         pytest.fail("libcf.so is not built (run __graft_entry__.build())")
-    lib = ctypes.CDLL(LIB)
+    return ctypes.CDLL(LIB)
+
+
+@pytest.fixture(scope="module")
+def L(lib):
+    """The library, for validation calls whose valid cases stop at the device check."""
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("valid calls with placeholder pointers would launch on a present GPU")
     return lib
 
 
@@ -42,9 +52,9 @@ def test_header_declares_the_entry_points():
         assert want in syms
 
 
-def test_every_declared_symbol_is_exported(L):
+def test_every_declared_symbol_is_exported(lib):
     for s in declared_symbols():
-        assert hasattr(L, s), f"{s} declared in include/ but not exported by libcf.so"
+        assert hasattr(lib, s), f"{s} declared in include/ but not exported by libcf.so"
 
 
 def test_no_torch_in_the_library():
@@ -53,21 +63,21 @@ def test_no_torch_in_the_library():
     assert "torch" not in out and "at::" not in out
 
 
-def test_strerror_and_version(L):
-    L.cf_strerror.restype = ctypes.c_char_p
+def test_strerror_and_version(lib):
+    lib.cf_strerror.restype = ctypes.c_char_p
     for code in range(0, -9, -1):
-        assert L.cf_strerror(code)
-    assert L.cf_abi_version() == 1
+        assert lib.cf_strerror(code)
+    assert lib.cf_abi_version() == 1
 
 
-def test_codes_bytes(L):
-    L.cf_codes_bytes.restype = ctypes.c_int64
-    L.cf_codes_bytes.argtypes = [ctypes.c_int64, ctypes.c_int]
-    assert L.cf_codes_bytes(1024 * 3072, 1) == 393216
-    assert L.cf_codes_bytes(1024 * 3072, 2) == 786432
-    assert L.cf_codes_bytes(2925 * 1920, 2) == 1404000
-    assert L.cf_codes_bytes(100, 1) == CF_E_SHAPE
-    assert L.cf_codes_bytes(128, 3) == CF_E_ARG
+def test_codes_bytes(lib):
+    lib.cf_codes_bytes.restype = ctypes.c_int64
+    lib.cf_codes_bytes.argtypes = [ctypes.c_int64, ctypes.c_int]
+    assert lib.cf_codes_bytes(1024 * 3072, 1) == 393216
+    assert lib.cf_codes_bytes(1024 * 3072, 2) == 786432
+    assert lib.cf_codes_bytes(2925 * 1920, 2) == 1404000
+    assert lib.cf_codes_bytes(100, 1) == CF_E_SHAPE
+    assert lib.cf_codes_bytes(128, 3) == CF_E_ARG
 
 
 def _compress(L, bits=1, dt=0, a=0x10000, ah=0x1000000, e=0x2000000, c=0x3000000, s=0x4000000,
