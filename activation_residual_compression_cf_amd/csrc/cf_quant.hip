@@ -23,7 +23,8 @@
 // Launch shape (measured on MI355X): the senders run one instruction per stream per
 // tile in one-wave blocks at every call size (2-3% faster than 256-thread blocks on a
 // whole FLUX step, 1.5% faster than two instructions per tile in 128-thread blocks on
-// one layer's K and V).  The decode of a whole step runs 256-thread blocks, its bf16
+// one layer's K and V), with their blocks renumbered into runs per XCD
+// (run_order_block, cf_vec.h).  The decode of a whole step runs 256-thread blocks, its bf16
 // variant one-wave blocks; a small decode call uses two instructions per tile and
 // 128-thread blocks, which keeps more bytes in flight per wave when the grid alone
 // cannot fill the chip for long.
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
     constexpr int kWaves = BLOCK / 64;
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;  // lane within the half wave that owns a group
-    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    const int64_t tile = static_cast<int64_t>(run_order_block<kRunWaves / kWaves>()) * kWaves + (threadIdx.x >> 6);
     const int64_t g0 = tile * (2 * IPS) + (lane >> 5);
     if (tile * (2 * IPS) >= ngroups) return;  // uniform per wave
 
@@ -171,7 +172,8 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
     }
 }
 
-template <int BITS, int IPS, int BLOCK, bool OUT16>
+// RUNS: blocks in runs per XCD (run_order_block), else in plain order.
+template <int BITS, int IPS, int BLOCK, bool OUT16, bool RUNS>
 __global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict__ codes,
                                                        const float* __restrict__ scales,
                                                        float* __restrict__ ahat, uint16_t* __restrict__ out,
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict_
     constexpr int kWaves = BLOCK / 64;
     const int lane = threadIdx.x & 63;
     const int hl = lane & 31;
-    const int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    const uint32_t block = run_order_block<RUNS ? kRunWaves / kWaves : 0>();
+    const int64_t tile = static_cast<int64_t>(block) * kWaves + (threadIdx.x >> 6);
     const int64_t g0 = tile * (2 * IPS) + (lane >> 5);
     if (tile * (2 * IPS) >= ngroups) return;
 
@@ -258,10 +261,10 @@ hipError_t run_decompress(const uint8_t* codes, const float* scales, float* ahat
     if (ngroups >= kLargeCall) {
         // the decode alone streams fastest in 256-thread blocks, with its bf16 copy in
         // one-wave blocks (FLUX step: 0.44 ms vs 0.45 ms, and 0.56 ms vs 0.57 ms)
-        if constexpr (OUT16) return launch(&k_decompress<BITS, 1, 64, OUT16>, ngroups, 1, 64, args, stream);
-        return launch(&k_decompress<BITS, 1, 256, OUT16>, ngroups, 1, 256, args, stream);
+        if constexpr (OUT16) return launch(&k_decompress<BITS, 1, 64, OUT16, true>, ngroups, 1, 64, args, stream);
+        return launch(&k_decompress<BITS, 1, 256, OUT16, true>, ngroups, 1, 256, args, stream);
     }
-    return launch(&k_decompress<BITS, 2, 128, OUT16>, ngroups, 2, 128, args, stream);
+    return launch(&k_decompress<BITS, 2, 128, OUT16, false>, ngroups, 2, 128, args, stream);
 }
 
 template <typename ActT>

@@ -1,5 +1,6 @@
 // Device helpers shared by the element-wise kernels: 4-wide fp32 vectors,
-// non-temporal loads and stores, bf16 widening and rounding.
+// non-temporal loads and stores, bf16 widening and rounding, and the block order of
+// the streaming kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,6 +39,35 @@ __device__ __forceinline__ float bf16_widen(uint32_t h) { return __uint_as_float
 // Round-to-nearest-even bf16 of 4 finite floats, packed as 2 words.
 __device__ __forceinline__ vu2 to_bf16x4(vf4 v) {
     return vu2{bf16_rne(v.x) | (bf16_rne(v.y) << 16), bf16_rne(v.z) | (bf16_rne(v.w) << 16)};
+}
+
+// Block order of the streaming kernels.  The hardware deals consecutive workgroups to
+// the eight XCDs in turn, so in plain order the code words and scales of one 128-byte
+// line are written (or read) by several L2s, each moving its own partial line (1.15%
+// more write traffic for the sender on a FLUX step).  Renumbered, block b, the j-th
+// (j = b / 8) dealt to XCD b % 8, takes block ((j / RUN) * 8 + b % 8) * RUN + j % RUN:
+// each XCD walks runs of RUN consecutive blocks, and the eight runs of one round lie
+// side by side, so lines stay whole while the chip's access front stays compact.
+// Blocks past the last whole round keep their own index; the map is a permutation of
+// [0, gridDim.x).  RUN = 0 keeps the plain order.  Measured on a FLUX step: runs of
+// 128 or 256 waves make the 1-bit sender (one-wave blocks) 1.5% faster than plain
+// order, with exactly the algorithmic writes, and the decode about 1.5% faster; runs
+// of 512 to 8192 waves are up to 2% slower, and one contiguous range per XCD 3% slower.
+// The top-k kernels, the warmup copy and the low-rank reconstruction, whose blocks
+// write whole lines anyway, measured no faster in runs and keep the plain order.
+constexpr uint32_t kRunWaves = 256;
+
+template <uint32_t RUN>
+__device__ __forceinline__ uint32_t run_order_block() {
+    const uint32_t b = blockIdx.x;
+    if constexpr (RUN == 0) {
+        return b;
+    } else {
+        constexpr uint32_t kRound = 8u * RUN;
+        if (b >= gridDim.x / kRound * kRound) return b;
+        const uint32_t j = b >> 3;
+        return ((j / RUN) * 8u + (b & 7u)) * RUN + j % RUN;
+    }
 }
 
 }  // namespace cf
