@@ -23,7 +23,8 @@
 // output slot.
 //
 // A wave takes kPerWave consecutive groups in straight-line code, with each group's loads
-// issued two groups ahead.  No memory operation sits under a data-dependent branch, so
+// issued two groups ahead.  Blocks of 8 waves take their groups in per-XCD runs
+// (kTopkRunWaves below).  No memory operation sits under a data-dependent branch, so
 // the compiler can wait for exactly the loads a group needs.  The payload of the wave's
 // groups is one contiguous span of the output (kPerWave*k index bytes, as many bf16
 // values).  It is staged in LDS and written as whole dwords once the wave is done; the
