@@ -78,6 +78,9 @@ def _ptr(t: torch.Tensor | None):
         return None
     if not t.is_cuda:
         raise ValueError("libcf takes device tensors (a host pointer would fault the kernel)")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()} "
+                         "(libcf launches on the current device)")
     if not t.is_contiguous():
         raise ValueError("libcf needs contiguous tensors")
     return ctypes.c_void_p(t.data_ptr())
@@ -152,6 +155,8 @@ def init_state(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None = N
     """Warmup: ahat = a, err = 0 (err None on the receiver)."""
     _dtype("ahat", ahat, _F32)
     _dtype("err", err, _F32)
+    _need("ahat", ahat, 4 * a.numel())
+    _need("err", err, 4 * a.numel())
     _check("cf_init_state", lib.cf_init_state(_act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err),
                                               a.numel(), _stream(stream)))
 

@@ -259,6 +259,22 @@ def test_binding_refuses_host_tensors():
         cf.topk_compress(4, a, ah, er, torch.zeros(8, dtype=torch.uint8), torch.zeros(8, dtype=torch.int16))
 
 
+def test_binding_refuses_short_state_buffers():
+    """Buffer sizes are invisible to the C ABI, so the binding compares them with what the
+    call writes before any call (here before it even looks at the device)."""
+    import torch
+
+    from activation_residual_compression_cf_amd import cf
+
+    a = torch.zeros(256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="ahat holds"):
+        cf.init_state(a, torch.zeros(128), torch.zeros(256))
+    with pytest.raises(ValueError, match="err holds"):
+        cf.init_state(a, torch.zeros(256), torch.zeros(255))
+    with pytest.raises(ValueError, match="codes holds"):
+        cf.compress(2, a, torch.zeros(256), torch.zeros(256), torch.zeros(32, dtype=torch.uint8), torch.zeros(2))
+
+
 def test_binding_refuses_wrong_element_types():
     """State and scales must be fp32, codes and index bytes uint8: the C ABI takes untyped
     pointers, so the binding refuses other element types before any call."""
