@@ -92,6 +92,19 @@ def test_several_tiles_ragged_tail(cf, dev, O, bits, dtype):
 
 
 @pytest.mark.parametrize("bits", [1, 2])
+@pytest.mark.parametrize("rows", [1567, 44001])
+def test_partial_round_of_block_runs(cf, dev, O, bits, rows):
+    """Grids that end inside a round of the per-XCD block runs, with a ragged last tile.
+    3 tensors of rows x 128 in one call: 1567 rows give 4701 groups, so the sender's
+    2351 one-wave blocks fill one round of 2048 and part of the next; 44001 rows give
+    132003 groups, enough for the decode's large launch (16501 blocks of 256 threads,
+    32 rounds of 512 and a partial one) and 66002 sender blocks (32 rounds of 2048 and
+    a partial one)."""
+    wl = gen.Workload(f"runs{rows}", rows, 128, 3, 4, "bf16", True)
+    run_trajectory(cf, dev, O, wl, bits, warmup=1, steps=4, per_call=3, samples=[0, 1, 2])
+
+
+@pytest.mark.parametrize("bits", [1, 2])
 def test_single_group_special_values(cf, dev, O, bits):
     """One group: zero residual, exact 2-bit ties, signed zeros, subnormals."""
     cases = []
@@ -124,9 +137,16 @@ def test_single_group_special_values(cf, dev, O, bits):
 
 def test_flux_1bit_full_shape(cf, dev, O):
     """114 x (1024 x 3072) bf16 per step, Compact-1bit, 1 warmup step, one call per
-    layer (K and V), as the benchmark times it."""
+    layer (K and V), as the benchmark's per-layer row times it."""
     run_trajectory(cf, dev, O, gen.WORKLOADS["flux"], 1, warmup=1, steps=3, per_call=2,
                    samples=[0, 1, 57, 113])
+
+
+def test_flux_1bit_full_shape_one_call(cf, dev, O):
+    """The benchmark's headline launch: Compact-1bit, the whole step of 114 tensors as
+    one call, 1 warmup step."""
+    run_trajectory(cf, dev, O, gen.WORKLOADS["flux"], 1, warmup=1, steps=3, per_call=114,
+                   samples=[0, 56, 113])
 
 
 def test_flux_2bit_full_shape_one_call(cf, dev, O):
