@@ -100,6 +100,30 @@ def test_step_parity_small(cf, dev, O, rank, iters, fb, dtype):
         prev = A
 
 
+@pytest.mark.parametrize("m,n,rank,iters,fb", [(2048, 16, 16, 2, 4), (16, 4096, 16, 2, 4),
+                                              (1040, 48, 10, 3, 32), (32, 528, 30, 1, 16),
+                                              (64, 64, 8, 64, 4)])
+def test_step_parity_extreme_shapes(cf, dev, O, m, n, rank, iters, fb):
+    """Tall and wide tensors (one column tile, one row tile, full rank = min(m, n)),
+    partial row and column tiles, and the most iterations a call takes (64); 2 tensors
+    per call, 2 steps."""
+    wl = gen.Workload("lrx", m, n, 2, 3, "bf16", True)
+    say(f"lowrank extreme shape: {m}x{n} rank={rank} iters={iters} fb={fb}")
+    tr = gen.Trajectory(wl, 3)
+    A0 = tr.next()
+    a0 = to_dev(A0, dev)
+    ahat = torch.empty((2, m, n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(a0, ahat, err)
+    qs = torch.from_numpy(start_bases(3, 2, n, rank)).to(dev)
+    prev = A0
+    for t in range(1, 3):
+        A = tr.next()
+        check_step(cf, dev, O, prev, A, ahat, err, qs, rank, iters, fb, samples=[0, 1],
+                   tol=2e-4 if fb == 32 else 1e-3)
+        prev = A
+
+
 def test_int4_stage_isolated(cf, dev, O):
     """The INT4 codes and scales equal the oracle's quantizer on the GPU's fp32 factors."""
     wl = gen.Workload("lr", 256, 768, 2, 2, "bf16", True)
