@@ -149,6 +149,14 @@ def test_flux_1bit_full_shape_one_call(cf, dev, O):
                    samples=[0, 56, 113])
 
 
+def test_flux_1bit_whole_trajectory(cf, dev, O):
+    """All 28 denoising steps of the FLUX shard (1 warmup, 27 compressed), the headline
+    launch, with two sampled tensors replayed on the oracle at every step: bit-exact
+    over the whole horizon, where the error feedback has had every step to accumulate."""
+    run_trajectory(cf, dev, O, gen.WORKLOADS["flux"], 1, warmup=1, steps=28, per_call=114,
+                   samples=[3, 110])
+
+
 def test_flux_2bit_full_shape_one_call(cf, dev, O):
     """Compact-2bit, 2 warmup steps, the whole step as one slab call."""
     run_trajectory(cf, dev, O, gen.WORKLOADS["flux"], 2, warmup=2, steps=4, per_call=114,

@@ -159,6 +159,12 @@ def test_flux_full_shape_one_call(cf, dev, O):
     run_topk(cf, dev, O, gen.WORKLOADS["flux"], 12, steps=3, samples=[0, 57, 113])
 
 
+def test_flux_whole_trajectory(cf, dev, O):
+    """All 28 denoising steps of the FLUX shard at k = 12, one call per step, two sampled
+    tensors replayed on the oracle at every step."""
+    run_topk(cf, dev, O, gen.WORKLOADS["flux"], 12, steps=28, samples=[9, 104])
+
+
 def test_cogvideo_full_shape(cf, dev, O):
     """60 tensors of 2925 x 1920 bf16 (CogVideoX-2b shard), k = 6."""
     run_topk(cf, dev, O, gen.WORKLOADS["cogvideo"], 6, steps=2, samples=[0, 59])
