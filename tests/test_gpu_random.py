@@ -1,0 +1,106 @@
+"""Randomised bit-exact parity of the 1/2-bit and top-k paths over wide value ranges.
+
+Each case draws its size, activation dtype, compressor and data from a seeded
+generator: per-group magnitudes spread over 60 decades of the fp32 exponent range
+(10^-30 to 10^30), reconstructions that sit close to the activation in some groups and
+are unrelated in others, and exact zeros, negative zeros and repeated values sprinkled
+in.  Sizes run from one group to a few thousand.  The GPU's codes, scales, index bytes,
+values, reconstruction, error and receiver mirror must equal the oracle's bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import host, mismatch, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+@pytest.fixture(scope="module")
+def cf():
+    from activation_residual_compression_cf_amd import cf as _cf
+
+    return _cf
+
+
+@pytest.fixture(scope="module")
+def dev(cf):
+    return cf.require_device()
+
+
+@pytest.fixture(scope="module")
+def O():
+    return oracle.default()
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even bf16 bits of finite fp32 values (the test's input encoding)."""
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _widen(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw_case(seed: int):
+    rng = np.random.default_rng(1000 + seed)
+    groups = int(rng.integers(1, 3000))
+    n = 128 * groups
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    mag = np.repeat(10.0 ** rng.uniform(-30, 30, size=groups), 128)
+    x = rng.standard_normal(n) * mag
+    u = rng.random(n)
+    x[u < 0.02] = 0.0
+    x[(u >= 0.02) & (u < 0.03)] = -0.0
+    rep = (u >= 0.03) & (u < 0.06)
+    x[rep] = mag[rep]  # ties inside a group
+    a32 = x.astype(np.float32)
+    a = _bf16_bits(a32) if dtype == "bf16" else a32
+    a_f = _widen(a) if dtype == "bf16" else a
+    # reconstruction: near the activation in half the groups, unrelated in the others
+    near = np.repeat(rng.random(groups) < 0.5, 128)
+    other = (rng.standard_normal(n) * np.repeat(10.0 ** rng.uniform(-30, 30, size=groups), 128))
+    ahat = np.where(near, a_f * (1 + 1e-3 * rng.standard_normal(n)), other).astype(np.float32)
+    kind = ("q1", "q2", "topk")[seed % 3]
+    k = {2: 1, 5: 128}.get(seed, int(rng.integers(1, 129)))
+    return n, dtype, a, ahat, kind, k
+
+
+def _same_bits(x: np.ndarray, y: np.ndarray) -> bool:
+    return np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_case(cf, dev, O, seed):
+    n, dtype, a, ahat0, kind, k = draw_case(seed)
+    say(f"random case {seed}: {kind} n={n} dtype={dtype}" + (f" k={k}" if kind == "topk" else ""))
+    ah_o, er_o, rx_o = ahat0.copy(), np.zeros(n, np.float32), ahat0.copy()
+    a_d = to_dev(a, dev)
+    ah_d, rx_d = to_dev(ahat0, dev), to_dev(ahat0, dev)
+    er_d = torch.full((n,), 7.0, device=dev)
+    if kind == "topk":
+        idx_o, vals_o = O.topk_compress(k, a, ah_o, er_o)
+        O.topk_decompress(k, idx_o, vals_o, rx_o)
+        idx, vals = cf.topk_compress(k, a_d, ah_d, er_d)
+        cf.topk_decompress(k, idx, vals, rx_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx), idx_o), mismatch(host(idx), idx_o)
+        assert np.array_equal(host(vals).view(np.uint16), vals_o), mismatch(host(vals).view(np.uint16), vals_o)
+    else:
+        bits = 1 if kind == "q1" else 2
+        codes_o, scales_o = O.compress(bits, a, ah_o, er_o)
+        O.decompress(bits, codes_o, scales_o, rx_o)
+        codes, scales = cf.compress(bits, a_d, ah_d, er_d)
+        cf.decompress(bits, codes, scales, rx_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(codes), codes_o), mismatch(host(codes), codes_o)
+        assert _same_bits(host(scales), scales_o), mismatch(host(scales), scales_o)
+    assert _same_bits(host(ah_d), ah_o), mismatch(host(ah_d).view(np.uint32), ah_o.view(np.uint32))
+    assert _same_bits(host(er_d), er_o), mismatch(host(er_d).view(np.uint32), er_o.view(np.uint32))
+    assert _same_bits(host(rx_d), rx_o), mismatch(host(rx_d).view(np.uint32), rx_o.view(np.uint32))
