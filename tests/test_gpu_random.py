@@ -1,11 +1,14 @@
-"""Randomised bit-exact parity of the 1/2-bit and top-k paths over wide value ranges.
+"""Randomised bit-exact parity of the 1/2-bit, top-k and ablation paths over wide value
+ranges.
 
 Each case draws its size, activation dtype, compressor and data from a seeded
 generator: per-group magnitudes spread over 60 decades of the fp32 exponent range
 (10^-30 to 10^30), reconstructions that sit close to the activation in some groups and
 are unrelated in others, and exact zeros, negative zeros and repeated values sprinkled
 in.  Sizes run from one group to a few thousand.  The GPU's codes, scales, index bytes,
-values, reconstruction, error and receiver mirror must equal the oracle's bit for bit.
+values, reconstruction, error and receiver mirror must equal the oracle's bit for bit;
+the ablation modes (no error feedback against a previous activation, naive quantization
+of the activation itself) compare their codes, scales and reconstruction.
 """
 from __future__ import annotations
 
@@ -18,7 +21,7 @@ from gpu_util import host, mismatch, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
-CASES = 24
+CASES = 30
 
 
 @pytest.fixture(scope="module")
@@ -67,9 +70,11 @@ def draw_case(seed: int):
     near = np.repeat(rng.random(groups) < 0.5, 128)
     other = (rng.standard_normal(n) * np.repeat(10.0 ** rng.uniform(-30, 30, size=groups), 128))
     ahat = np.where(near, a_f * (1 + 1e-3 * rng.standard_normal(n)), other).astype(np.float32)
-    kind = ("q1", "q2", "topk")[seed % 3]
-    k = {2: 1, 5: 128}.get(seed, int(rng.integers(1, 129)))
-    return n, dtype, a, ahat, kind, k
+    kind = ("q1", "q2", "topk", "noef", "naive")[seed % 5]
+    k = {2: 1, 7: 128}.get(seed, int(rng.integers(1, 129)))
+    prev = a_f * (1 + 1e-2 * rng.standard_normal(n))  # the previous step's activation
+    a_prev = _bf16_bits(prev.astype(np.float32)) if dtype == "bf16" else prev.astype(np.float32)
+    return n, dtype, a, ahat, kind, k, a_prev
 
 
 def _same_bits(x: np.ndarray, y: np.ndarray) -> bool:
@@ -78,8 +83,23 @@ def _same_bits(x: np.ndarray, y: np.ndarray) -> bool:
 
 @pytest.mark.parametrize("seed", range(CASES))
 def test_random_case(cf, dev, O, seed):
-    n, dtype, a, ahat0, kind, k = draw_case(seed)
+    n, dtype, a, ahat0, kind, k, a_prev = draw_case(seed)
     say(f"random case {seed}: {kind} n={n} dtype={dtype}" + (f" k={k}" if kind == "topk" else ""))
+    if kind in ("noef", "naive"):
+        bits = 1 + seed % 2
+        ah_o = ahat0.copy()
+        a_d, ah_d = to_dev(a, dev), to_dev(ahat0, dev)
+        if kind == "noef":
+            codes_o, scales_o = O.compress_noef(bits, a, a_prev, ah_o)
+            codes, scales = cf.compress_ablation(cf.CF_MODE_NOEF, bits, a_d, ah_d, to_dev(a_prev, dev))
+        else:
+            ah_o, codes_o, scales_o = O.quantize_naive(bits, a)
+            codes, scales = cf.compress_ablation(cf.CF_MODE_NAIVE, bits, a_d, ah_d)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(codes), codes_o), mismatch(host(codes), codes_o)
+        assert _same_bits(host(scales), scales_o), mismatch(host(scales), scales_o)
+        assert _same_bits(host(ah_d), ah_o), mismatch(host(ah_d).view(np.uint32), ah_o.view(np.uint32))
+        return
     ah_o, er_o, rx_o = ahat0.copy(), np.zeros(n, np.float32), ahat0.copy()
     a_d = to_dev(a, dev)
     ah_d, rx_d = to_dev(ahat0, dev), to_dev(ahat0, dev)
