@@ -6,7 +6,8 @@ generator: per-group magnitudes spread over 60 decades of the fp32 exponent rang
 (10^-30 to 10^30), reconstructions that sit close to the activation in some groups and
 are unrelated in others, and exact zeros, negative zeros and repeated values sprinkled
 in.  Sizes run from one group to a few thousand.  The GPU's codes, scales, index bytes,
-values, reconstruction, error and receiver mirror must equal the oracle's bit for bit;
+values, reconstruction, error and receiver mirror (and, for half the quantizer cases, the
+mirror's round-to-nearest-even bf16 copy) must equal the oracle's bit for bit;
 the ablation modes (no error feedback against a previous activation, naive quantization
 of the activation itself) compare their codes, scales and reconstruction.
 """
@@ -117,10 +118,15 @@ def test_random_case(cf, dev, O, seed):
         codes_o, scales_o = O.compress(bits, a, ah_o, er_o)
         O.decompress(bits, codes_o, scales_o, rx_o)
         codes, scales = cf.compress(bits, a_d, ah_d, er_d)
-        cf.decompress(bits, codes, scales, rx_d)
+        # even seeds decode with the bf16 copy of the mirror (cf_decompress_bf16)
+        out16 = torch.empty(n, dtype=torch.bfloat16, device=dev) if seed % 2 == 0 else None
+        cf.decompress(bits, codes, scales, rx_d, out_bf16=out16)
         torch.cuda.synchronize()
         assert np.array_equal(host(codes), codes_o), mismatch(host(codes), codes_o)
         assert _same_bits(host(scales), scales_o), mismatch(host(scales), scales_o)
+        if out16 is not None:
+            got16 = host(out16.view(torch.int16)).view(np.uint16)
+            assert np.array_equal(got16, _bf16_bits(rx_o)), mismatch(got16, _bf16_bits(rx_o))
     assert _same_bits(host(ah_d), ah_o), mismatch(host(ah_d).view(np.uint32), ah_o.view(np.uint32))
     assert _same_bits(host(er_d), er_o), mismatch(host(er_d).view(np.uint32), er_o.view(np.uint32))
     assert _same_bits(host(rx_d), rx_o), mismatch(host(rx_d).view(np.uint32), rx_o.view(np.uint32))
