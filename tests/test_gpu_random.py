@@ -130,3 +130,58 @@ def test_random_case(cf, dev, O, seed):
     assert _same_bits(host(ah_d), ah_o), mismatch(host(ah_d).view(np.uint32), ah_o.view(np.uint32))
     assert _same_bits(host(er_d), er_o), mismatch(host(er_d).view(np.uint32), er_o.view(np.uint32))
     assert _same_bits(host(rx_d), rx_o), mismatch(host(rx_d).view(np.uint32), rx_o.view(np.uint32))
+
+
+LOWRANK_CASES = 12
+
+
+def draw_lowrank_case(seed: int):
+    rng = np.random.default_rng(2000 + seed)
+    m, n = 16 * int(rng.integers(1, 40)), 16 * int(rng.integers(1, 40))
+    fb = (4, 16, 32)[seed % 3]
+    rank = int(rng.integers(1, min(m, n, 64) + 1))
+    if fb == 4:
+        rank = max(2, rank - rank % 2)
+    iters = int(rng.integers(1, 7))
+    batch = int(rng.integers(1, 4))
+    dtype = "bf16" if seed % 2 == 0 else "f32"
+    scale = 10.0 ** rng.uniform(-8, 8, size=(batch, 1, 1))
+    a32 = (rng.standard_normal((batch, m, n)) * scale).astype(np.float32)
+    a = _bf16_bits(a32) if dtype == "bf16" else a32
+    a_f = _widen(a) if dtype == "bf16" else a
+    ahat = (a_f * (1 + 0.1 * rng.standard_normal((batch, m, n)))).astype(np.float32)
+    q = rng.standard_normal((batch, n, rank)).astype(np.float32)
+    return m, n, rank, iters, fb, batch, dtype, a, ahat, q
+
+
+def _rel(x, y):
+    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
+    ny = np.linalg.norm(y)
+    return np.linalg.norm(x - y) / (ny if ny > 0 else 1.0)
+
+
+@pytest.mark.parametrize("seed", range(LOWRANK_CASES))
+def test_random_lowrank_case(cf, dev, O, seed):
+    """Random shapes (multiples of 16 up to 624), ranks, iteration counts, factor widths,
+    batches and per-tensor magnitudes (10^-8 to 10^8): the reconstruction update agrees
+    with the oracle's to the low-rank tolerance, e == a - Ahat exactly, and the receiver
+    equals the sender bit for bit."""
+    m, n, rank, iters, fb, batch, dtype, a, ahat0, q0 = draw_lowrank_case(seed)
+    say(f"random low-rank case {seed}: {batch} x {m}x{n} rank={rank} iters={iters} fb={fb} dtype={dtype}")
+    a_d, ah_d, rx_d = to_dev(a, dev), to_dev(ahat0, dev), to_dev(ahat0, dev)
+    er_d = torch.empty_like(ah_d)
+    q_d = to_dev(q0, dev)
+    payload = cf.lowrank_compress(a_d, ah_d, er_d, q_d, rank, iters, fb)
+    cf.lowrank_decompress(fb, payload, rx_d, rank)
+    torch.cuda.synchronize()
+    assert torch.equal(rx_d, ah_d), "receiver differs from sender"
+    assert torch.equal(er_d, a_d.float() - ah_d), "err != a - ahat"
+    tol = 2e-4 if fb == 32 else 1e-3
+    for s in range(batch):
+        ah_o, er_o, q_o = ahat0[s].copy(), np.zeros((m, n), np.float32), q0[s].copy()
+        O.lowrank_compress(np.ascontiguousarray(a[s]), ah_o, er_o, q_o, rank, iters, fb)
+        r_gpu = host(ah_d[s]).astype(np.float64) - ahat0[s]
+        r_orc = ah_o.astype(np.float64) - ahat0[s]
+        e = _rel(r_gpu, r_orc)
+        say(f"  tensor {s}: rel(R_gpu, R_oracle) = {e:.2e}")
+        assert e <= tol, f"tensor {s}: reconstruction update differs by {e:.3e}"
