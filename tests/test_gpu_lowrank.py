@@ -19,7 +19,7 @@ import torch
 
 import gen
 import oracle
-from gpu_util import host, say, to_dev
+from gpu_util import explain_int4_ties, host, rel, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,52 +41,8 @@ def O():
     return oracle.default()
 
 
-def rel(a, b):
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    nb = np.linalg.norm(b)
-    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
-
-
 def start_bases(seed, slots, n, rank):
     return np.stack([gen.start_basis(seed, s, n, rank) for s in range(slots)])
-
-
-# An INT4 code is decided by rint(x / s) in fp32 on both sides, but the fp32 factor x
-# itself is only determined to about 1e-6 relative (Householder QR in fp64 against
-# Cholesky QR with fp32 MFMA products).  Where x / s lies that close to a half-integer,
-# both neighbouring codes are valid roundings, and one flipped code can move the
-# reconstruction by a few 1e-3 of its norm (one outer product of a factor column).
-TIE = 1e-4  # |x / s - (j + 1/2)| below which either rounding is accepted
-
-
-def int4_codes(O, packed, rows, k):
-    return O.int4_dequantize(packed, np.ones(k, np.float32), rows, k).astype(np.int32)
-
-
-def explain_int4_ties(O, a, ah_before, q_before, rank, iters, gpu_pay, r_gpu, tol):
-    """Where the GPU's INT4 codes differ from the oracle's, the oracle's own fp32 factor
-    must sit at a rounding tie and the codes must be neighbours; the GPU's reconstruction
-    must then equal the oracle's reconstruction of those codes with the oracle's scales.
-    Returns (number of tie flips, that relative error)."""
-    m, n = ah_before.shape
-    er = np.zeros_like(ah_before)
-    P, _, Q, _ = O.lowrank_compress(a, ah_before.copy(), er, q_before.copy(), rank, iters, 32)
-    u_o, us_o, v_o, vs_o = O.lowrank_compress(a, ah_before.copy(), er, q_before.copy(), rank, iters, 4)
-    u_g, us_g, v_g, vs_g = gpu_pay
-    assert rel(us_g, us_o) <= 1e-5 and rel(vs_g, vs_o) <= 1e-5, "INT4 scales differ"
-    flips = 0
-    for X, sc, po, pg, rows in ((P, us_o, u_o, u_g, m), (Q, vs_o, v_o, v_g, n)):
-        co, cg = int4_codes(O, po, rows, rank), int4_codes(O, pg, rows, rank)
-        diff = co != cg
-        if diff.any():
-            t = (np.asarray(X, np.float32).reshape(rows, rank)[diff] / sc[np.nonzero(diff)[1]]).astype(np.float32)
-            assert np.all(np.abs(co[diff] - cg[diff]) == 1), "INT4 codes differ by more than one step"
-            assert np.all(np.abs(np.abs(t - np.trunc(t)) - 0.5) <= TIE), "INT4 codes differ away from a tie"
-            flips += int(diff.sum())
-    r_ties = np.zeros((m, n), np.float32)
-    O.lowrank_decompress(4, u_g, us_o, v_g, vs_o, r_ties, rank)
-    return flips, rel(r_gpu, r_ties)
 
 
 def check_step(cf, dev, O, A_prev_host, A_host, ahat_d, err_d, qs_d, rank, iters, fb, samples,

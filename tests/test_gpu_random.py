@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import host, mismatch, say, to_dev
+from gpu_util import explain_int4_ties, host, mismatch, rel, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -154,18 +154,13 @@ def draw_lowrank_case(seed: int):
     return m, n, rank, iters, fb, batch, dtype, a, ahat, q
 
 
-def _rel(x, y):
-    x, y = np.asarray(x, np.float64), np.asarray(y, np.float64)
-    ny = np.linalg.norm(y)
-    return np.linalg.norm(x - y) / (ny if ny > 0 else 1.0)
-
-
 @pytest.mark.parametrize("seed", range(LOWRANK_CASES))
 def test_random_lowrank_case(cf, dev, O, seed):
     """Random shapes (multiples of 16 up to 624), ranks, iteration counts, factor widths,
     batches and per-tensor magnitudes (10^-8 to 10^8): the reconstruction update agrees
-    with the oracle's to the low-rank tolerance, e == a - Ahat exactly, and the receiver
-    equals the sender bit for bit."""
+    with the oracle's to the low-rank tolerance (INT4 codes at rounding ties accepted as in
+    the trajectory tests), e == a - Ahat exactly, and the receiver equals the sender bit
+    for bit."""
     m, n, rank, iters, fb, batch, dtype, a, ahat0, q0 = draw_lowrank_case(seed)
     say(f"random low-rank case {seed}: {batch} x {m}x{n} rank={rank} iters={iters} fb={fb} dtype={dtype}")
     a_d, ah_d, rx_d = to_dev(a, dev), to_dev(ahat0, dev), to_dev(ahat0, dev)
@@ -182,6 +177,14 @@ def test_random_lowrank_case(cf, dev, O, seed):
         O.lowrank_compress(np.ascontiguousarray(a[s]), ah_o, er_o, q_o, rank, iters, fb)
         r_gpu = host(ah_d[s]).astype(np.float64) - ahat0[s]
         r_orc = ah_o.astype(np.float64) - ahat0[s]
-        e = _rel(r_gpu, r_orc)
+        e = rel(r_gpu, r_orc)
         say(f"  tensor {s}: rel(R_gpu, R_oracle) = {e:.2e}")
+        if e > tol and fb == 4:
+            u, us, v, vs = (host(x) for x in payload)
+            hu, hv = m * rank // 2, n * rank // 2
+            gpu_pay = (u[s * hu:(s + 1) * hu], us[s * rank:(s + 1) * rank],
+                       v[s * hv:(s + 1) * hv], vs[s * rank:(s + 1) * rank])
+            flips, e = explain_int4_ties(O, np.ascontiguousarray(a[s]), ahat0[s], q0[s], rank, iters,
+                                         gpu_pay, r_gpu, tol)
+            say(f"  tensor {s}: {flips} INT4 codes at rounding ties; with them rel = {e:.2e}")
         assert e <= tol, f"tensor {s}: reconstruction update differs by {e:.3e}"
