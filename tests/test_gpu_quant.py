@@ -163,6 +163,14 @@ def test_flux_2bit_full_shape_one_call(cf, dev, O):
                    samples=[0, 77, 113])
 
 
+def test_cogvideo_2bit_whole_trajectory(cf, dev, O):
+    """All 50 CogVideoX-2b shard steps (2 warmup, 48 compressed) of 60 tensors of
+    2925 x 1920, Compact-2bit, the whole step as one call; two sampled tensors replayed
+    on the oracle at every step."""
+    run_trajectory(cf, dev, O, gen.WORKLOADS["cogvideo"], 2, warmup=2, steps=50, per_call=60,
+                   samples=[1, 58])
+
+
 def test_cogvideo_2bit_full_shape(cf, dev, O):
     """60 x (2925 x 1920) bf16 per step, Compact-2bit, 2 warmup steps."""
     run_trajectory(cf, dev, O, gen.WORKLOADS["cogvideo"], 2, warmup=2, steps=4, per_call=2,
