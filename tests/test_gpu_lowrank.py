@@ -266,7 +266,9 @@ def test_flux_shape(cf, dev, O, rank, iters):
         prev = A
 
 
-@pytest.mark.parametrize("rank,iters,samples", [(32, 2, list(range(8))), (8, 10, [0, 5])])
+# slots 0 and 6 each hold one INT4 code at a rounding tie at some step (see
+# explain_int4_ties); slot 7 comes closest to the bar without one
+@pytest.mark.parametrize("rank,iters,samples", [(32, 2, [0, 6, 7]), (8, 10, [0, 5])])
 def test_flux_whole_trajectory(cf, dev, O, rank, iters, samples):
     """All 28 FLUX steps (1 warmup, 27 compressed) of 114 tensors per call with INT4
     factors and the warm-started basis carried from step to step; sampled tensors are
