@@ -20,8 +20,8 @@
  * The pages fix neither group size, scale rule, code layout nor precision; the
  * readings taken here are:
  *   - groups of 128 contiguous elements; 1-bit: code = (r < 0), scale = mean|r|
- *     (summed as 32 left-to-right partial sums of 4 elements, combined by the
- *     butterfly L_j += L_{j^o}, o = 16, 8, 4, 2, 1, then divided by 128);
+ *     taken exactly and rounded once to fp32 (to nearest, ties to even), which
+ *     leaves no summation order to choose;
  *     2-bit: scale s = max|r| / 1.5, levels {-1.5, -0.5, 0.5, 1.5} * s chosen
  *     by round-to-nearest with ties to the inner level, code bit0 = sign,
  *     bit1 = magnitude; codes packed LSB-first, 8 or 4 per byte;
@@ -33,7 +33,9 @@
  *     low-rank linear algebra (projections, Householder QR, reconstruction
  *     sums) runs in fp64 and rounds to fp32 where a value is stored;
  *   - low rank: P = orth(r Q) (thin Householder QR, diag(R) >= 0, columns with
- *     |R_jj| <= 1e-12 ||Y||_F set to zero), Q = r^T P, repeated `iters` times;
+ *     |R_jj| <= 1e-5 ||Y||_F set to zero: the residual is fp32, so a column of Y
+ *     that small relative to the whole sits at the level of fp32 rounding noise,
+ *     and counts as rank-deficient), Q = r^T P, repeated `iters` times;
  *     INT4 factors use per-column absmax scales s = max|x| / 7 and codes
  *     rint(x / s) clamped to [-7, 7], two's-complement nibbles, low nibble
  *     first along the rank index; 16-bit factors (the table's "Pure Lowrank")
@@ -93,19 +95,49 @@ static int check_common(int bits, int dtype, int64_t numel) {
  * sender and the receiver use one and the same expression.
  * ------------------------------------------------------------------------- */
 
-/* 1-bit scale: mean of |r| in the fixed summation order described above. */
+/* 1-bit scale: the mean of |r| over the group, taken exactly and rounded once to
+ * fp32 (to nearest, ties to even).
+ * Every finite fp32 value is a whole number of units of 2^-149, so the sum of the
+ * 128 magnitudes is a whole number N of those units, below 2^285.  N is held in
+ * nine 32-bit words, least significant first; the mean is N * 2^-156. */
+#define CFO_SUM_WORDS 9
+
+static int sum_bit(const uint32_t* N, int b) { return (int)((N[b >> 5] >> (b & 31)) & 1u); }
+
 static float scale_1bit(const float* r) {
-    float L[32], nxt[32];
-    for (int j = 0; j < 32; ++j) {
-        float s = fabsf(r[4 * j]);
-        for (int i = 1; i < 4; ++i) s = s + fabsf(r[4 * j + i]);
-        L[j] = s;
+    uint32_t N[CFO_SUM_WORDS] = {0};
+    for (int i = 0; i < CFO_GROUP; ++i) {
+        float x = fabsf(r[i]);
+        uint32_t u;
+        memcpy(&u, &x, 4);
+        uint32_t expo = u >> 23, mant = u & 0x7FFFFFu;
+        /* normal: (mant + 2^23) * 2^(expo - 150);  subnormal: mant * 2^-149 */
+        uint64_t units = expo ? (uint64_t)(mant | 0x800000u) : mant;
+        int shift = expo ? (int)expo - 1 : 0; /* x = units * 2^(shift - 149) */
+        /* add units << shift to N, word by word, carrying upwards */
+        int w = shift / 32;
+        uint64_t add = units << (shift % 32); /* below 2^55: words w and w + 1 */
+        uint64_t carry = 0;
+        for (int j = w; j < CFO_SUM_WORDS; ++j) {
+            uint64_t t = (uint64_t)N[j] + (add & 0xFFFFFFFFu) + carry;
+            N[j] = (uint32_t)t;
+            carry = t >> 32;
+            add >>= 32;
+        }
     }
-    for (int o = 16; o >= 1; o >>= 1) {
-        for (int j = 0; j < 32; ++j) nxt[j] = L[j] + L[j ^ o];
-        memcpy(L, nxt, sizeof L);
-    }
-    return L[0] / 128.0f;
+    int top = -1; /* highest set bit of N */
+    for (int b = 32 * CFO_SUM_WORDS - 1; b >= 0 && top < 0; --b)
+        if (sum_bit(N, b)) top = b;
+    if (top < 0) return 0.0f;
+    /* N * 2^-156 as q * 2^(low - 156): keep 24 significant bits, or fewer when the
+     * mean is subnormal (its last bit is worth 2^-149, bit 7 of N). */
+    int low = top - 23 > 7 ? top - 23 : 7;
+    uint32_t q = 0;
+    for (int b = top; b >= low; --b) q = (q << 1) | (uint32_t)sum_bit(N, b);
+    int half = sum_bit(N, low - 1), rest = 0;
+    for (int b = low - 2; b >= 0; --b) rest |= sum_bit(N, b);
+    if (half && (rest || (q & 1u))) q += 1; /* to nearest, ties to even */
+    return ldexpf((float)q, low - 156);
 }
 
 /* 2-bit scale: largest |r| mapped onto the outer level 1.5 s. */
@@ -303,7 +335,7 @@ int cfo_int4_dequantize(const uint8_t* packed, const float* scales, int64_t rows
 
 /* Thin Householder QR of Y (m x k, row-major, fp64): P (m x k) with
  * orthonormal columns spanning Y's, signs chosen so diag(R) >= 0, and columns
- * whose |R_jj| <= 1e-12 ||Y||_F set to zero.  alive[j] reports which survive. */
+ * whose |R_jj| <= 1e-5 ||Y||_F set to zero.  alive[j] reports which survive. */
 static int householder_orth(const double* Y, int64_t m, int k, double* P, int* alive) {
     double* A = (double*)malloc(sizeof(double) * (size_t)(m * k));
     double* V = (double*)calloc((size_t)(m * k), sizeof(double)); /* reflector j in column j */
@@ -349,7 +381,7 @@ static int householder_orth(const double* Y, int64_t m, int k, double* P, int* a
     }
     for (int j = 0; j < k; ++j) {
         double rj = j < steps ? rdiag[j] : 0.0;
-        alive[j] = fabs(rj) > 1e-12 * fro;
+        alive[j] = fabs(rj) > 1e-5 * fro;
         double sgn = rj < 0.0 ? -1.0 : 1.0;
         for (int64_t i = 0; i < m; ++i) P[i * k + j] = alive[j] ? sgn * P[i * k + j] : 0.0;
     }

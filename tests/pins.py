@@ -19,6 +19,7 @@ from __future__ import annotations
 import dataclasses
 import os
 import sys
+from fractions import Fraction
 
 import numpy as np
 
@@ -107,6 +108,78 @@ def pin_golden_q1(O):
 
 def pin_golden_q2(O):
     _golden_group(O, "q2_group.txt")
+
+
+def _golden_floats(tokens) -> np.ndarray:
+    """Hexadecimal floats, with "n*x" standing for n copies of x."""
+    out = []
+    for tok in tokens:
+        n, _, x = tok.rpartition("*")
+        out += [float.fromhex(x)] * (int(n) if n else 1)
+    return np.array(out, np.float32)
+
+
+def pin_golden_q1_exact_mean(O):
+    """Hand-derived 1-bit scales at rounding ties, a tie broken by a tiny term,
+    subnormal means and a sum beyond fp32's range (tests/golden/q1_exact_mean.txt)."""
+    g = load_golden("q1_exact_mean.txt")
+    for case in sorted({k.split("_")[0] for k in g}):
+        a = np.zeros(128, np.float32)
+        r = _golden_floats(g[f"{case}_r"])
+        a[: r.size] = r
+        _, scales = O.compress(1, a, np.zeros(128, np.float32), np.zeros(128, np.float32))
+        want = int(g[f"{case}_scale_bits"][0], 16)
+        got = int(scales.view(np.uint32)[0])
+        assert got == want, f"{case}: scale bits {got:08x}, want {want:08x}"
+
+
+def _nearest_f32(x: Fraction) -> int:
+    """Bit pattern of the fp32 nearest to the exact rational x >= 0, ties to the even
+    significand: a brute-force search over the neighbours of x's fp64 rounding."""
+    c = int(np.float32(float(x)).view(np.uint32))
+    best = None
+    for u in range(max(c - 2, 0), min(c + 2, 0x7F7FFFFF) + 1):
+        d = abs(Fraction(float(np.uint32(u).view(np.float32))) - x)
+        if best is None or (d, u & 1) < best[0]:
+            best = ((d, u & 1), u)
+    return best[1]
+
+
+def _q1_test_groups(rng) -> np.ndarray:
+    """Groups of 128 residual magnitudes that stress the rounding of the mean: smooth
+    data over many decades, integer grids whose sums often sit exactly halfway
+    between two fp32 values, the same with a far smaller term that breaks the tie,
+    subnormals, and spans of up to 2^250 within one group."""
+    G = []
+    for _ in range(64):  # Gaussian groups, one magnitude per group
+        G.append(rng.standard_normal(128) * 10.0 ** rng.uniform(-30, 30))
+    for _ in range(64):  # integers near 2^19: 27-bit sums, ties in about 1 of 8
+        G.append(rng.integers(2 ** 18, 2 ** 20, 128).astype(np.float64) * 2.0 ** rng.integers(-60, 60))
+    for _ in range(64):  # the same with one term 2^-40 .. 2^-120 of the rest
+        g = rng.integers(2 ** 18, 2 ** 20, 128).astype(np.float64)
+        g[rng.integers(128)] = 2.0 ** -rng.integers(21, 101)
+        G.append(g * 2.0 ** rng.integers(-20, 20))
+    for _ in range(32):  # subnormal sums
+        G.append(rng.integers(0, 2 ** 12, 128).astype(np.float64) * 2.0 ** -149)
+    for _ in range(32):  # wide spans inside one group, a few exact zeros
+        g = rng.standard_normal(128) * 2.0 ** rng.integers(-149, 100, 128)
+        g[rng.integers(128, size=4)] = 0.0
+        G.append(g)
+    return np.clip(np.stack(G), -3e38, 3e38).astype(np.float32)
+
+
+def pin_q1_exact_mean(O):
+    """The 1-bit scale is the exact mean of |r| over the group rounded once to fp32
+    (nearest, ties to even), checked with exact rational arithmetic."""
+    rng = np.random.default_rng(21)
+    r = _q1_test_groups(rng)
+    a = r.reshape(-1).copy()
+    _, scales = O.compress(1, a, np.zeros_like(a), np.zeros_like(a))
+    got = scales.view(np.uint32)
+    for g in range(r.shape[0]):
+        exact = sum((Fraction(float(abs(x))) for x in r[g]), Fraction(0)) / 128
+        want = _nearest_f32(exact)
+        assert int(got[g]) == want, f"group {g}: scale bits {int(got[g]):08x}, want {want:08x}"
 
 
 def pin_golden_int4(O):
@@ -222,7 +295,7 @@ def pin_q1_least_squares(O):
     rhs = (rg ** 2).sum(1) - np.abs(rg).sum(1) ** 2 / 128
     assert np.allclose(lhs, rhs, rtol=1e-5, atol=1e-6 * (rg ** 2).sum(1).max())
     s64 = np.abs(rg).mean(1)
-    assert np.all(np.abs(scales - s64) <= 64 * np.spacing(scales))
+    assert np.all(np.abs(scales - s64) <= np.spacing(scales)), "scale more than 1 ulp from the mean"
     g = rng.standard_normal(n).astype(np.float32)
     ah = np.zeros(n, np.float32)
     e2 = np.zeros(n, np.float32)
@@ -374,6 +447,33 @@ def pin_lowrank_planted(O):
     u, us, v, vs = O.lowrank_compress(a, ahat, err, q, k, 1, 32)
     assert np.linalg.norm(ahat - r) / np.linalg.norm(r) <= 1e-5
     assert np.count_nonzero(np.abs(u).sum(0)) == k0, "rank-deficient columns are zeroed"
+
+
+def pin_lowrank_rank_guard(O):
+    """The orthonormalisation treats a column of Y = rQ whose |R_jj| is at most
+    1e-5 ||Y||_F as rank-deficient: its P column is zero, and q_state keeps that
+    column's start vector.  Planted spectrum 1, 1e-3, 1e-7, 1e-9 with the start basis
+    on the right singular vectors, so |R_jj| / ||Y||_F follows the spectrum."""
+    rng = np.random.default_rng(15)
+    m, n, k = 64, 48, 4
+    U, _ = np.linalg.qr(rng.standard_normal((m, k)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    sig = np.array([1.0, 1e-3, 1e-7, 1e-9])
+    for scale in (1.0, 2.0 ** -40, 2.0 ** 40):
+        r = (((U * sig) @ V.T) * scale).astype(np.float32)
+        q0 = V.astype(np.float32)
+        q = q0.copy()
+        ahat = np.zeros_like(r)
+        err = np.zeros_like(r)
+        u, _, v, _ = O.lowrank_compress(r.copy(), ahat, err, q, k, 1, 32)
+        live = np.abs(u).sum(0) > 0
+        assert live.tolist() == [True, True, False, False], live
+        assert not v[:, 2:].any(), "a dead column sends a zero V column"
+        assert np.array_equal(q[:, 2:], q0[:, 2:]), "dead columns keep their start vector"
+        assert np.array_equal(q[:, :2], v[:, :2]), "live columns carry the new Q"
+        rhat = u.astype(np.float64) @ v.astype(np.float64).T
+        want = (U[:, :2] * sig[:2]) @ V[:, :2].T * scale
+        assert np.linalg.norm(rhat - want) <= 1e-6 * np.linalg.norm(want)
 
 
 def pin_lowrank_eckart_young(O):

@@ -29,9 +29,15 @@ MUTANTS = [
     ("residual_drops_ahat",
      "for (int i = 0; i < CFO_GROUP; ++i) r[i] = act(dtype, a, base + i) - ahat[base + i];",
      "for (int i = 0; i < CFO_GROUP; ++i) r[i] = act(dtype, a, base + i);"),
-    ("q1_mean_divisor", "return L[0] / 128.0f;", "return L[0] / 127.0f;"),
-    ("q1_butterfly_index", "nxt[j] = L[j] + L[j ^ o];", "nxt[j] = L[j] + L[j ^ (o >> 1)];"),
-    ("q1_partial_sum_stride", "s = s + fabsf(r[4 * j + i]);", "s = s + fabsf(r[4 * i + j]);"),
+    ("q1_mean_divisor", "return ldexpf((float)q, low - 156);", "return ldexpf((float)q, low - 155);"),
+    ("q1_implicit_bit", "(uint64_t)(mant | 0x800000u)", "(uint64_t)mant"),
+    ("q1_exponent_offset", "int shift = expo ? (int)expo - 1 : 0;", "int shift = expo ? (int)expo : 0;"),
+    ("q1_carry_dropped", "carry = t >> 32;\n            add >>= 32;", "carry = 0;\n            add >>= 32;"),
+    ("q1_signed_sum", "float x = fabsf(r[i]);\n        uint32_t u;", "float x = r[i] < 0.0f ? 0.0f : r[i];\n        uint32_t u;"),
+    ("q1_ties_away", "if (half && (rest || (q & 1u))) q += 1;", "if (half) q += 1;"),
+    ("q1_sticky_ignored", "if (half && (rest || (q & 1u))) q += 1;", "if (half && (q & 1u)) q += 1;"),
+    ("q1_truncates", "if (half && (rest || (q & 1u))) q += 1;", "(void)half; (void)rest;"),
+    ("q1_subnormal_last_bit", "int low = top - 23 > 7 ? top - 23 : 7;", "int low = top - 23 > 6 ? top - 23 : 6;"),
     ("q1_code_sign", "c = r[i] < 0.0f ? 1u : 0u;", "c = r[i] > 0.0f ? 1u : 0u;"),
     ("q1_bit_order", "gcodes[i >> 3] |= (uint8_t)(c << (i & 7));",
      "gcodes[i >> 3] |= (uint8_t)(c << (7 - (i & 7)));"),
@@ -56,7 +62,8 @@ MUTANTS = [
      "packed[(i * k + j) / 2] |= (uint8_t)((j & 1) ? nib : nib << 4);"),
     ("int4_sign_extend", "int c = nib >= 8 ? nib - 16 : nib;", "int c = nib;"),
     ("householder_beta", "beta[j] = 2.0 / vv;", "beta[j] = 1.0 / vv;"),
-    ("householder_guard", "alive[j] = fabs(rj) > 1e-12 * fro;", "alive[j] = fabs(rj) > 1e-2 * fro;"),
+    ("householder_guard_high", "alive[j] = fabs(rj) > 1e-5 * fro;", "alive[j] = fabs(rj) > 1e-2 * fro;"),
+    ("householder_guard_low", "alive[j] = fabs(rj) > 1e-5 * fro;", "alive[j] = fabs(rj) > 1e-12 * fro;"),
     ("householder_reverse_order", "for (int j = steps - 1; j >= 0; --j) {",
      "for (int j = 0; j < steps; ++j) {"),
     ("backproject_column", "for (int j = 0; j < k; ++j) Q[l * k + j] += ril * P[i * k + j];",
