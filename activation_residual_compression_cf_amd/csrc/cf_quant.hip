@@ -11,9 +11,10 @@
 // [256k, 256k + 256) of the tile: lane j holds the 4 consecutive elements
 // 256k + 4j .. 256k + 4j + 3, so every load and store instruction touches one
 // contiguous span (1 KiB of fp32 state, 512 B of bf16 activation) and each half
-// wave (32 lanes) owns one whole group of 128 elements.  The group reduction
-// (sum or max of |r|) is a 5-step xor butterfly (16, 8, 4, 2, 1) inside the half
-// wave; every lane ends with the same value.  Activations and state are read, and
+// wave (32 lanes) owns one whole group of 128 elements.  The group reductions (max
+// of |r|; for 1-bit also the exact sum that gives the mean) run inside the half wave,
+// four steps by DPP within rows of 16 lanes and one lane exchange between the two
+// rows; every lane ends with the same value.  Activations and state are read, and
 // state written, with non-temporal accesses: each byte is touched once per step,
 // so nothing is worth keeping in L2 and the end-of-kernel write-back stays short.
 // One pass per element: the activation and reconstruction are read once, the
@@ -38,10 +39,161 @@
 namespace cf {
 namespace {
 
-// Value held by lane (this lane ^ mask) / (this lane + delta), as 32-bit words.
+// Value held by lane (this lane ^ mask), through the LDS crossbar.
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
-__device__ __forceinline__ uint32_t down_lane(uint32_t v, int delta) {
-    return static_cast<uint32_t>(__shfl_down(static_cast<int>(v), delta, 64));
+
+// Lane moves inside a row of 16 lanes by DPP, an operand modifier of the VALU: no LDS
+// traffic and a few cycles of latency, against a ds_bpermute round trip.  Reduction
+// partners: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i of 8 with lane 7 - i, in the other quad) and row_mirror
+// (lane i of 16 with lane 15 - i, in the other half row); after those four steps every
+// lane of a row has combined all 16.  row_shl:d gives lane i the value of lane i + d of
+// its row; a lane whose source lies past the row's end keeps its own value.
+enum : int {
+    kDppXor1 = 0xB1,
+    kDppXor2 = 0x4E,
+    kDppHalfMirror = 0x141,
+    kDppMirror = 0x140,
+    kDppShl1 = 0x101,
+    kDppShl2 = 0x102,
+    kDppShl4 = 0x104,
+};
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __uint_as_float(dpp<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint64_t lo = dpp<CTRL>(static_cast<uint32_t>(u)), hi = dpp<CTRL>(static_cast<uint32_t>(u >> 32));
+    return __longlong_as_double(static_cast<long long>((hi << 32) | lo));
+}
+
+// max over the 32 lanes of a half wave, the same value in each of them (max is exact,
+// so the order of the steps does not matter)
+__device__ __forceinline__ float half_wave_max(float M) {
+    M = fmaxf(M, dpp<kDppXor1>(M));
+    M = fmaxf(M, dpp<kDppXor2>(M));
+    M = fmaxf(M, dpp<kDppHalfMirror>(M));
+    M = fmaxf(M, dpp<kDppMirror>(M));
+    return fmaxf(M, xor_lane(M, 16));
+}
+
+// ---------------------------------------------------------------------------------
+// 1-bit group scale: the mean of |r| over the half wave's group of 128, taken exactly
+// and rounded once to fp32 (to nearest, ties to even).  That value is unique, so no
+// summation order is involved.
+//
+// Fast path.  With M = max|r| in [2^p, 2^(p+1)), every |r_i| is cut down to a whole
+// multiple of u = 2^(p-43) (y_i = |r_i| / u < 2^44, f_i = floor(y_i)).  The f_i are
+// integers and their sum stays below 2^51, so it is exact in fp64 in any order, and
+// V = u * sum(f_i) / 128 is exact as well.  The exact mean lies in [V, V + u/128).
+// When no |r_i| lost bits to the cut, the mean is V and its fp32 rounding is final.
+// Otherwise fp32(V) is final when fp32(V + u/128) equals it: rounding is monotone.
+// Only when the cut bits could move the rounding across a boundary (never seen on
+// activation residuals; it takes terms below 2^-43 of the group's largest and a sum
+// within 2^-50 of it from a rounding boundary) does the exact slow path run.
+
+// Adds |x| (any fp32 bit pattern, taken as a whole number of units of 2^-149) to
+// the 288-bit integer held in w[0..8], least significant word first.
+__device__ __forceinline__ void add_units(uint32_t (&w)[9], float x) {
+    const uint32_t u = __float_as_uint(x) & 0x7FFFFFFFu;
+    const uint32_t e = u >> 23;
+    const uint64_t m = e ? ((u & 0x7FFFFFu) | 0x800000u) : (u & 0x7FFFFFu);
+    const uint32_t sh = e ? e - 1 : 0;  // |x| = m * 2^(sh - 149), sh <= 254
+    const uint64_t v = m << (sh & 31);  // below 2^55: words sh/32 and sh/32 + 1
+    const uint32_t at = sh >> 5, lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+    uint64_t c = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < 9; ++k) {
+        const uint32_t add = k == at ? lo : (k == at + 1 ? hi : 0u);
+        c += static_cast<uint64_t>(w[k]) + add;
+        w[k] = static_cast<uint32_t>(c);
+        c >>= 32;
+    }
+}
+
+__device__ __forceinline__ uint32_t word_at(const uint32_t (&w)[9], int k) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) out = j == k ? w[j] : out;
+    return out;
+}
+
+// Slow path: the exact sum of the group's |r| as a 288-bit integer in units of
+// 2^-149 (each lane adds its four, then an xor butterfly adds the half wave's
+// lanes with carries), then N * 2^-156 rounded to fp32 by hand.  Every lane of the
+// half wave must take part; all of them return the same value.
+__device__ __noinline__ float group_mean_abs_exact(float x0, float x1, float x2, float x3) {
+    uint32_t w[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    add_units(w, x0);
+    add_units(w, x1);
+    add_units(w, x2);
+    add_units(w, x3);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+        uint32_t other[9];
+#pragma unroll
+        for (int k = 0; k < 9; ++k) other[k] = static_cast<uint32_t>(__shfl_xor(static_cast<int>(w[k]), o, 64));
+        uint64_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            c += static_cast<uint64_t>(w[k]) + other[k];
+            w[k] = static_cast<uint32_t>(c);
+            c >>= 32;
+        }
+    }
+    int top = -1;  // highest set bit
+#pragma unroll
+    for (int k = 8; k >= 0; --k)
+        if (top < 0 && w[k] != 0) top = 32 * k + 31 - __clz(static_cast<int>(w[k]));
+    if (top < 0) return 0.0f;
+    // keep 24 significant bits, or fewer when the mean is subnormal (its last bit,
+    // 2^-149, is bit 7 of N)
+    const int low = top - 23 > 7 ? top - 23 : 7;
+    const uint64_t win = static_cast<uint64_t>(word_at(w, low >> 5)) |
+                         (static_cast<uint64_t>(word_at(w, (low >> 5) + 1)) << 32);
+    uint32_t q = static_cast<uint32_t>(win >> (low & 31));  // bits low..top; higher bits are 0
+    const int hb = low - 1;                                  // the half-unit bit, >= 6
+    const uint32_t half = (word_at(w, hb >> 5) >> (hb & 31)) & 1u;
+    uint32_t rest = word_at(w, hb >> 5) & ((1u << (hb & 31)) - 1u);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) rest |= k < (hb >> 5) ? w[k] : 0u;
+    if (half && (rest || (q & 1u))) q += 1u;  // to nearest, ties to even
+    return ldexpf(static_cast<float>(q), low - 156);
+}
+
+// The half wave's group of 128 |r| (four per lane): its exact mean rounded once to
+// fp32, the same value in every lane of the half wave.
+__device__ __forceinline__ float group_mean_abs(const vf4 r, int lane) {
+    const float x0 = fabsf(r.x), x1 = fabsf(r.y), x2 = fabsf(r.z), x3 = fabsf(r.w);
+    const float M = half_wave_max(fmaxf(fmaxf(x0, x1), fmaxf(x2, x3)));
+    const int p = __builtin_amdgcn_frexp_expf(M) - 1;  // M in [2^p, 2^(p+1)); M = 0 gives p = -1
+    const double y0 = ldexp(static_cast<double>(x0), 43 - p), y1 = ldexp(static_cast<double>(x1), 43 - p);
+    const double y2 = ldexp(static_cast<double>(x2), 43 - p), y3 = ldexp(static_cast<double>(x3), 43 - p);
+    const double f0 = floor(y0), f1 = floor(y1), f2 = floor(y2), f3 = floor(y3);
+    const bool cut = (f0 != y0) | (f1 != y1) | (f2 != y2) | (f3 != y3);
+    // whole numbers below 2^53: every sum is exact, in any order
+    double L = (f0 + f1) + (f2 + f3);
+    L = L + dpp<kDppXor1>(L);
+    L = L + dpp<kDppXor2>(L);
+    L = L + dpp<kDppHalfMirror>(L);
+    L = L + dpp<kDppMirror>(L);
+    L = L + __shfl_xor(L, 16, 64);
+    const double V = ldexp(L, p - 50);
+    float s = static_cast<float>(V);
+    const uint64_t cuts = __ballot(cut);
+    const uint32_t mine = (lane & 32) ? static_cast<uint32_t>(cuts >> 32) : static_cast<uint32_t>(cuts);
+    if (mine != 0u) {  // the same branch in every lane of the half wave
+        if (static_cast<float>(V + ldexp(1.0, p - 50)) != s) s = group_mean_abs_exact(x0, x1, x2, x3);
+    }
+    return s;
 }
 
 // Decoded value of one code (the expression shared by sender and receiver).
@@ -105,25 +257,11 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
         float s;
         uint32_t code;
         if constexpr (BITS == 1) {
-            float L = fabsf(r.x);
-            L = L + fabsf(r.y);
-            L = L + fabsf(r.z);
-            L = L + fabsf(r.w);
-            L = L + xor_lane(L, 16);
-            L = L + xor_lane(L, 8);
-            L = L + xor_lane(L, 4);
-            L = L + xor_lane(L, 2);
-            L = L + xor_lane(L, 1);
-            s = L / 128.0f;
+            s = group_mean_abs(r, lane);
             code = (r.x < 0.0f ? 1u : 0u) | (r.y < 0.0f ? 2u : 0u) | (r.z < 0.0f ? 4u : 0u) |
                    (r.w < 0.0f ? 8u : 0u);
         } else {
-            float M = fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w)));
-            M = fmaxf(M, xor_lane(M, 16));
-            M = fmaxf(M, xor_lane(M, 8));
-            M = fmaxf(M, xor_lane(M, 4));
-            M = fmaxf(M, xor_lane(M, 2));
-            M = fmaxf(M, xor_lane(M, 1));
+            const float M = half_wave_max(fmaxf(fmaxf(fabsf(r.x), fabsf(r.y)), fmaxf(fabsf(r.z), fabsf(r.w))));
             s = M / 1.5f;
             code = 0;
 #pragma unroll
@@ -145,15 +283,16 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
         }
 
         // Gather the group's codes into dwords: 1-bit lanes hold a nibble (8 lanes
-        // per dword), 2-bit lanes a byte (4 lanes per dword).
+        // per dword), 2-bit lanes a byte (4 lanes per dword).  The lanes that store a
+        // dword (every 8th or 4th) read only lanes of their own row of 16.
         uint32_t w;
         if constexpr (BITS == 1) {
-            w = code | (down_lane(code, 1) << 4);
-            w = w | (down_lane(w, 2) << 8);
-            w = w | (down_lane(w, 4) << 16);
+            w = code | (dpp<kDppShl1>(code) << 4);
+            w = w | (dpp<kDppShl2>(w) << 8);
+            w = w | (dpp<kDppShl4>(w) << 16);
         } else {
-            w = code | (down_lane(code, 1) << 8);
-            w = w | (down_lane(w, 2) << 16);
+            w = code | (dpp<kDppShl1>(code) << 8);
+            w = w | (dpp<kDppShl2>(w) << 16);
         }
 
         if (ok[k]) {
