@@ -113,6 +113,20 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream))
 
 
+def _keep_for(t: torch.Tensor | None, stream) -> torch.Tensor | None:
+    """Tie a buffer this module allocated (on the current stream) to the launch stream.
+    PyTorch's caching allocator may hand a freed block to new work on the stream it was
+    allocated on at once; when the kernels run on another stream, record_stream makes it
+    wait for that stream's work first."""
+    if t is None or stream is None:
+        return t
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    if stream.cuda_stream != torch.cuda.current_stream().cuda_stream:
+        t.record_stream(stream)
+    return t
+
+
 def _act_dtype(a: torch.Tensor) -> int:
     if a.dtype == torch.bfloat16:
         return CF_BF16
@@ -167,9 +181,9 @@ def compress(bits: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor |
     err None skips the (diagnostic) error buffer."""
     n = a.numel()
     if codes is None:
-        codes = torch.empty(max(n * bits // 8, 0), dtype=torch.uint8, device=a.device)
+        codes = _keep_for(torch.empty(max(n * bits // 8, 0), dtype=torch.uint8, device=a.device), stream)
     if scales is None:
-        scales = torch.empty(max(n // GROUP, 0), dtype=torch.float32, device=a.device)
+        scales = _keep_for(torch.empty(max(n // GROUP, 0), dtype=torch.float32, device=a.device), stream)
     for nm, t, dt in (("ahat", ahat, _F32), ("err", err, _F32), ("codes", codes, _U8), ("scales", scales, _F32)):
         _dtype(nm, t, dt)
     for nm, t, nb in (("ahat", ahat, 4 * n), ("err", err, 4 * n), ("codes", codes, n * bits // 8),
@@ -205,9 +219,9 @@ def compress_ablation(mode: int, bits: int, a: torch.Tensor, ahat: torch.Tensor,
     """Ablation sender step (CF_MODE_NOEF needs a_prev); returns (codes, scales)."""
     n = a.numel()
     if codes is None:
-        codes = torch.empty(n * bits // 8, dtype=torch.uint8, device=a.device)
+        codes = _keep_for(torch.empty(n * bits // 8, dtype=torch.uint8, device=a.device), stream)
     if scales is None:
-        scales = torch.empty(n // GROUP, dtype=torch.float32, device=a.device)
+        scales = _keep_for(torch.empty(n // GROUP, dtype=torch.float32, device=a.device), stream)
     for nm, t, dt in (("ahat", ahat, _F32), ("a_prev", a_prev, a.dtype), ("codes", codes, _U8),
                       ("scales", scales, _F32)):
         _dtype(nm, t, dt)
@@ -225,9 +239,9 @@ def topk_compress(k: int, a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor
     """One top-k sender step; returns (idx uint8[numel/128*k], vals bf16 bits int16[numel/128*k])."""
     slots = max(a.numel() // GROUP * k, 0)
     if idx is None:
-        idx = torch.empty(slots, dtype=torch.uint8, device=a.device)
+        idx = _keep_for(torch.empty(slots, dtype=torch.uint8, device=a.device), stream)
     if vals is None:
-        vals = torch.empty(slots, dtype=torch.int16, device=a.device)
+        vals = _keep_for(torch.empty(slots, dtype=torch.int16, device=a.device), stream)
     n = a.numel()
     for nm, t, dts in (("ahat", ahat, (_F32,)), ("err", err, (_F32,)), ("idx", idx, (_U8,)), ("vals", vals, _BITS16)):
         _dtype(nm, t, *dts)
@@ -378,11 +392,12 @@ def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | No
     (u, u_scales, v, v_scales).  q_state is (batch, n, rank) fp32, updated in place."""
     batch, m, n = a.shape
     if payload is None:
-        payload = lowrank_payload(batch, m, n, rank, factor_bits, a.device)
+        payload = tuple(_keep_for(t, stream) for t in lowrank_payload(batch, m, n, rank, factor_bits, a.device))
     u, us, v, vs = payload
     need = lowrank_workspace_bytes(m, n, rank, batch)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=a.device)
+        # freed when this call returns, possibly before the launch stream has used it
+        workspace = _keep_for(torch.empty(need, dtype=torch.uint8, device=a.device), stream)
     _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload)
     numel = batch * m * n
     for nm, t in (("ahat", ahat), ("err", err), ("q_state", q_state)):

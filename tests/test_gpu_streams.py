@@ -64,3 +64,42 @@ def test_two_streams_match_one_stream(cf):
         results.append([x.clone() for x in (*s1, c1, sc1, *s2, c2, sc2, *sk, ik, vk, *sl, ql, *pay)])
     for x, y in zip(*results):
         assert torch.equal(x, y)
+
+
+def test_side_stream_call_with_its_own_workspace(cf):
+    """The binding allocates the low-rank workspace (and payload) itself, launches on a
+    side stream and frees the workspace when the call returns.  Memory the current stream
+    allocates and fills straight after the call must not be that workspace while the side
+    stream still uses it: the results equal those of the same call with a workspace
+    allocated up front."""
+    dev = cf.require_device()
+    B, m, n, k = 8, 1024, 3072, 32
+    wl = gen.Workload("ws", m, n, B, 2, "bf16", True)
+    tr = gen.Trajectory(wl, 3)
+    A0, A1 = (to_dev(tr.next(), dev).view(B, m, n) for _ in range(2))
+    q0 = torch.from_numpy(np.stack([gen.start_basis(3, s, n, k) for s in range(B)])).to(dev)
+    need = cf.lowrank_workspace_bytes(m, n, k, B)
+    say("low rank on a side stream with the binding's own workspace")
+    outs = []
+    for own in (False, True):
+        ah = torch.empty((B, m, n), dtype=torch.float32, device=dev)
+        er = torch.empty_like(ah)
+        cf.init_state(A0, ah, er)
+        q = q0.clone()
+        torch.cuda.synchronize()
+        if not own:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            pay = cf.lowrank_compress(A1, ah, er, q, k, 2, 4, workspace=ws)
+            torch.cuda.synchronize()
+        else:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            pay = cf.lowrank_compress(A1, ah, er, q, k, 2, 4, stream=side)
+            junk = [torch.empty(need, dtype=torch.uint8, device=dev) for _ in range(2)]
+            for j in junk:
+                j.fill_(0xFF)  # NaN patterns wherever the workspace was reused too early
+            torch.cuda.synchronize()
+            del junk
+        outs.append([ah.clone(), er.clone(), q.clone(), *[p.clone() for p in pay]])
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
