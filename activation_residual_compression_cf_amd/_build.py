@@ -17,7 +17,9 @@ FLAGS = [
     "-shared",
     # one rounding per fp32 operation, in the order written (no FMA contraction)
     "-ffp-contract=off",
-    # no packed-fp32 instructions in device code
+    # no packed-fp32 instructions (v_pk_add/mul/fma_f32) in device code.  The feature
+    # applies to the gfx950 pass; the x86 host pass does not know it and warns that it
+    # ignores it, which is expected.  tests/test_build_flags.py reads the disassembly.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
