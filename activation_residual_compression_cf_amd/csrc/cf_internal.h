@@ -45,9 +45,12 @@ struct LowrankWorkspace {
 // Largest rank the low-rank kernels accept.
 constexpr int kMaxRank = 64;
 
-// Fills the region pointers for `base` (may be null) and the total size in *bytes.
+// Fills the region pointers of one launch sequence over `batch` tensors for `base` (may
+// be null) and its size in *bytes.
 LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch,
                                          size_t* bytes);
+// Workspace bytes of a whole call (a large call runs two halves, each with its own regions).
+size_t lowrank_workspace_total(int64_t m, int64_t n, int rank, int64_t batch);
 // Whether every launch of one low-rank call (or of its receiver) fits a dispatch.
 bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch);
 hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m,

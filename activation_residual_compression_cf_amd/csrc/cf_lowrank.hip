@@ -2,11 +2,11 @@
 // INT4 factors, error feedback, and the receiver-side reconstruction, for gfx950.
 //
 // Method: "Accelerating Parallel Diffusion Model Serving with Residual
-// Compression" (CompactFusion summary): section Approach (low-rank compression of
-// the step-wise residual with INT4 quantization for extreme ratios, sender-side
-// error feedback), Key results (rank 32 with INT4 factors, about 100x), the
-// measured-effects table (2 vs 10 subspace iterations) and Experimental setup,
-// "Builds on" (PowerSGD-style subspace iteration).
+// Compression" (CompactFusion summary): section Approach (the low-rank variant
+// factors the step's residual and quantizes both factors to INT4; the sender's error
+// feedback is the same as for the quantizers), Key results (the compression ratio
+// reached at rank 32), the measured-effects table (2 against 10 subspace iterations)
+// and Experimental setup, "Builds on" (subspace iteration as in PowerSGD).
 //
 // Per tensor (m x n, row-major), with Q the n x k start basis:
 //   r = a - Ahat                                   (fp32, kept in the workspace)
@@ -1046,10 +1046,12 @@ hipError_t launch_reconstruct(int factor_bits, int k, int64_t total, void** args
     return launch_reconstruct_fb<HAS_E, ActT, 32>(k, total, args, stream);
 }
 
+// One call's kernels for `batch` tensors on one stream.  With `after_first` set, that
+// event is recorded on the stream right after the first projection.
 template <typename ActT, int KT>
 hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_t n, int k, int iters,
                        int factor_bits, int64_t batch, float* q_state, void* u, float* u_scales, void* v,
-                       float* v_scales, const LowrankWorkspace& ws, hipStream_t stream) {
+                       float* v_scales, const LowrankWorkspace& ws, hipStream_t stream, hipEvent_t after_first) {
     const LowrankGrids grid = lowrank_grids(m, n, k, batch);
     int64_t nseg = grid.nseg;
     hipError_t e;
@@ -1064,6 +1066,7 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         e = it == 0 ? go(&k_lr_project<true, ActT, KT>, ptotal, pargs, stream)
                     : go(&k_lr_project<false, ActT, KT>, ptotal, pargs, stream);
         if (e != hipSuccess) return e;
+        if (it == 0 && after_first && (e = hipEventRecord(after_first, stream)) != hipSuccess) return e;
         int64_t gblocks = grid.gblocks;
         void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch};
         if ((e = go(&k_lr_gram<KT>, grid.gram, gargs, stream)) != hipSuccess) return e;
@@ -1100,16 +1103,99 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
 template <typename ActT>
 hipError_t dispatch_rank(const ActT* a, float* ahat, float* err, int64_t m, int64_t n, int k, int iters,
                          int factor_bits, int64_t batch, float* q_state, void* u, float* u_scales, void* v,
-                         float* v_scales, const LowrankWorkspace& ws, hipStream_t stream) {
+                         float* v_scales, const LowrankWorkspace& ws, hipStream_t stream, hipEvent_t after_first) {
     switch ((k + 15) / 16) {
-        case 1: return run_lowrank<ActT, 1>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream);
-        case 2: return run_lowrank<ActT, 2>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream);
-        case 3: return run_lowrank<ActT, 3>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream);
-        default: return run_lowrank<ActT, 4>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream);
+        case 1: return run_lowrank<ActT, 1>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream, after_first);
+        case 2: return run_lowrank<ActT, 2>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream, after_first);
+        case 3: return run_lowrank<ActT, 3>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream, after_first);
+        default: return run_lowrank<ActT, 4>(a, ahat, err, m, n, k, iters, factor_bits, batch, q_state, u, u_scales, v, v_scales, ws, stream, after_first);
     }
 }
 
+// ------------------------------------------------------- two halves, two streams --
+// A large call runs its tensors as two halves: the first on the caller's stream, the
+// second on a side stream that starts once the first half's first projection is done.
+// The halves then stand about one streaming pass apart, so the latency-bound kernels of
+// one (orthonormalisation, factor quantization) run while the other streams r, and the
+// ramp and drain of each pass overlaps the other half's work.  Each tensor's arithmetic
+// is the same as in one launch sequence, so the results are identical.  The side
+// stream has the default priority; the caller's stream waits for it before the call's
+// later work.  Calls below this size run as one sequence: the event round trips would
+// cost more than the overlap gains.
+constexpr int64_t kSplitElems = int64_t(1) << 24;
+
+// Tensors in the first half, or 0 for one sequence.
+int64_t split_first_half(int64_t m, int64_t n, int64_t batch) {
+    return batch >= 2 && m * n * batch >= kSplitElems ? (batch + 1) / 2 : 0;
+}
+
+// The side stream and the two events of one host thread on one device, made on first use
+// (with that device current) and kept for the life of the thread.  One set per thread, so
+// calls from several host threads never share an event.
+struct SplitSync {
+    hipStream_t side = nullptr;
+    hipEvent_t first_done = nullptr, second_done = nullptr;
+    hipError_t err = hipSuccess;
+    bool made = false;
+};
+constexpr int kMaxSplitDevices = 64;
+thread_local SplitSync t_split[kMaxSplitDevices];
+
+hipError_t split_sync(SplitSync** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxSplitDevices) return hipErrorInvalidDevice;
+    SplitSync& s = t_split[dev];
+    if (!s.made) {
+        s.made = true;
+        s.err = hipStreamCreateWithFlags(&s.side, hipStreamNonBlocking);
+        if (s.err == hipSuccess) s.err = hipEventCreateWithFlags(&s.first_done, hipEventDisableTiming);
+        if (s.err == hipSuccess) s.err = hipEventCreateWithFlags(&s.second_done, hipEventDisableTiming);
+    }
+    *out = &s;
+    return s.err;
+}
+
+template <typename ActT>
+hipError_t run_split(const ActT* a, float* ahat, float* err, int64_t m, int64_t n, int k, int iters, int factor_bits,
+                     int64_t batch, float* q_state, void* u, float* u_scales, void* v, float* v_scales,
+                     void* workspace, int64_t half, hipStream_t stream) {
+    SplitSync* sync = nullptr;
+    hipError_t e = split_sync(&sync);
+    if (e != hipSuccess) return e;
+    size_t bytes_first = 0;
+    const LowrankWorkspace ws1 = carve_lowrank_workspace(workspace, m, n, k, half, &bytes_first);
+    const LowrankWorkspace ws2 =
+        carve_lowrank_workspace(static_cast<char*>(workspace) + bytes_first, m, n, k, batch - half, nullptr);
+    const int64_t mn = m * n, fb8 = factor_bits;  // factor bits per (row, rank) pair
+    if ((e = dispatch_rank(a, ahat, err, m, n, k, iters, factor_bits, half, q_state, u, u_scales, v, v_scales, ws1,
+                           stream, sync->first_done)) != hipSuccess)
+        return e;
+    if ((e = hipStreamWaitEvent(sync->side, sync->first_done, 0)) != hipSuccess) return e;
+    if ((e = dispatch_rank(a + half * mn, ahat + half * mn, err ? err + half * mn : nullptr, m, n, k, iters,
+                           factor_bits, batch - half, q_state + half * n * k,
+                           static_cast<char*>(u) + half * m * k * fb8 / 8, u_scales ? u_scales + half * k : nullptr,
+                           static_cast<char*>(v) + half * n * k * fb8 / 8, v_scales ? v_scales + half * k : nullptr,
+                           ws2, sync->side, nullptr)) != hipSuccess)
+        return e;
+    if ((e = hipEventRecord(sync->second_done, sync->side)) != hipSuccess) return e;
+    return hipStreamWaitEvent(stream, sync->second_done, 0);
+}
+
 }  // namespace
+
+size_t lowrank_workspace_total(int64_t m, int64_t n, int rank, int64_t batch) {
+    size_t one = 0, two = 0;
+    const int64_t half = split_first_half(m, n, batch);
+    if (!half) {
+        carve_lowrank_workspace(nullptr, m, n, rank, batch, &one);
+        return one;
+    }
+    carve_lowrank_workspace(nullptr, m, n, rank, half, &one);
+    carve_lowrank_workspace(nullptr, m, n, rank, batch - half, &two);
+    return one + two;
+}
 
 LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch, size_t* bytes) {
     const int64_t kp = (rank + 15) / 16 * 16;
@@ -1159,12 +1245,19 @@ hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, floa
                                    int rank, int iters, int factor_bits, int64_t batch, float* q_state, void* u,
                                    float* u_scales, void* v, float* v_scales, void* workspace,
                                    hipStream_t stream) {
+    if (const int64_t half = split_first_half(m, n, batch)) {
+        if (a_dtype == 0)
+            return run_split(static_cast<const uint16_t*>(a), ahat, err, m, n, rank, iters, factor_bits, batch,
+                             q_state, u, u_scales, v, v_scales, workspace, half, stream);
+        return run_split(static_cast<const float*>(a), ahat, err, m, n, rank, iters, factor_bits, batch, q_state, u,
+                         u_scales, v, v_scales, workspace, half, stream);
+    }
     const LowrankWorkspace ws = carve_lowrank_workspace(workspace, m, n, rank, batch, nullptr);
     if (a_dtype == 0)
         return dispatch_rank(static_cast<const uint16_t*>(a), ahat, err, m, n, rank, iters, factor_bits, batch,
-                             q_state, u, u_scales, v, v_scales, ws, stream);
+                             q_state, u, u_scales, v, v_scales, ws, stream, nullptr);
     return dispatch_rank(static_cast<const float*>(a), ahat, err, m, n, rank, iters, factor_bits, batch, q_state,
-                         u, u_scales, v, v_scales, ws, stream);
+                         u, u_scales, v, v_scales, ws, stream, nullptr);
 }
 
 hipError_t launch_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,

@@ -92,3 +92,50 @@ def test_topk_graph_matches_eager(cf):
         torch.cuda.synchronize()
         for x, y in zip(st["graph"], st["eager"]):
             assert torch.equal(x, y), f"replay {t} differs from the eager run"
+
+
+def test_lowrank_split_call_graph_matches_eager(cf):
+    """A low-rank call large enough to run as two halves on two streams, captured into a
+    graph (the library's side stream joins the capture through its events) and replayed
+    on successive steps: every replay equals an eager run bit for bit."""
+    import numpy as np
+
+    dev = cf.require_device()
+    B, m, n, k = 8, 1024, 3072, 32  # 25M elements: two halves of 4 tensors
+    wl = gen.Workload("graphlr", m, n, B, 4, "bf16", True)
+    tr = gen.Trajectory(wl, 13)
+    A = [to_dev(tr.next(), dev).view(B, m, n) for _ in range(wl.steps)]
+    q0 = torch.from_numpy(np.stack([gen.start_basis(13, s, n, k) for s in range(B)])).to(dev)
+    say("graph capture of a two-stream low-rank call")
+    st = {}
+    for name in ("eager", "graph", "first"):
+        ah = torch.empty((B, m, n), dtype=torch.float32, device=dev)
+        er = torch.empty_like(ah)
+        cf.init_state(A[0], ah, er)
+        ws = torch.empty(cf.lowrank_workspace_bytes(m, n, k, B), dtype=torch.uint8, device=dev)
+        st[name] = (ah, er, q0.clone(), cf.lowrank_payload(B, m, n, k, 4, dev), ws)
+    # one eager call on this thread before the capture: the side stream and events of
+    # the split are made then, not during the capture
+    f = st.pop("first")
+    cf.lowrank_compress(A[1], f[0], f[1], f[2], k, 2, 4, f[3], f[4])
+    torch.cuda.synchronize()
+    del f
+    static_a = torch.empty_like(A[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    ah, er, q, pay, ws = st["graph"]
+    with torch.cuda.graph(g, stream=side):
+        cf.lowrank_compress(static_a, ah, er, q, k, 2, 4, pay, ws)
+    torch.cuda.synchronize()
+    for t in range(1, wl.steps):
+        static_a.copy_(A[t])
+        g.replay()
+        e = st["eager"]
+        cf.lowrank_compress(A[t], e[0], e[1], e[2], k, 2, 4, e[3], e[4])
+        junk = (A[t].float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        gx, ex = st["graph"], st["eager"]
+        for x, y in zip((gx[0], gx[1], gx[2], *gx[3]), (ex[0], ex[1], ex[2], *ex[3])):
+            assert torch.equal(x, y), f"replay {t} differs from the eager run"
