@@ -44,11 +44,13 @@ def rel(a, b):
 
 
 # An INT4 code is decided by rint(x / s) in fp32 on both sides, but the fp32 factor x
-# itself is only determined to about 1e-6 relative (Householder QR in fp64 against
-# Cholesky QR with fp32 MFMA products).  Where x / s lies that close to a half-integer,
-# both neighbouring codes are valid roundings, and one flipped code can move the
-# reconstruction by a few 1e-3 of its norm (one outer product of a factor column).
-TIE = 1e-4  # |x / s - (j + 1/2)| below which either rounding is accepted
+# itself is only determined to about 1e-6 of its column's largest element (Householder
+# QR in fp64 against Cholesky QR with fp32 MFMA products), and so is s = max|x| / 7.
+# With |x / s| <= 7 the two sides' x / s then differ by at most about 7 * 1e-6.  Where
+# x / s lies that close to a half-integer, both neighbouring codes are valid roundings,
+# and one flipped code can move the reconstruction by a few 1e-3 of its norm (one outer
+# product of a factor column).
+TIE = 1e-5  # |x / s - (j + 1/2)| below which either rounding is accepted
 
 
 def int4_codes(O, packed, rows, k):

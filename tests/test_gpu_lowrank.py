@@ -226,6 +226,47 @@ def test_planted_rank_and_zero_residual(cf, dev):
     assert np.array_equal(host(qs), q0)
 
 
+@pytest.mark.parametrize("fb", [32, 4])
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -60, 2.0 ** 40])
+def test_rank_guard_band(cf, dev, O, fb, scale):
+    """Columns of Y = rQ in the band between fp32 noise and a real direction.  Planted
+    residual with singular values 1, 1e-3, 1e-7, 1e-9 (times `scale`) and the start
+    basis on its right singular vectors, one iteration, so |R_jj| / ||Y||_F follows the
+    spectrum.  Both sides keep the first two columns and treat the last two as
+    rank-deficient (|R_jj| <= 1e-5 ||Y||_F): zero factor columns, and q_state keeps
+    their start vectors; the live columns of q_state and the reconstruction agree with
+    the oracle."""
+    rng = np.random.default_rng(15)
+    m, n, k = 64, 128, 4
+    U, _ = np.linalg.qr(rng.standard_normal((m, k)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, k)))
+    sig = np.array([1.0, 1e-3, 1e-7, 1e-9])
+    r = (((U * sig) @ V.T) * scale).astype(np.float32)
+    q0 = V.astype(np.float32)
+    say(f"rank guard band: fb={fb} scale=2^{int(np.log2(scale))}")
+    ahat = torch.zeros((1, m, n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    qs = to_dev(q0[None], dev)
+    u, _, v, _ = cf.lowrank_compress(to_dev(r[None], dev), ahat, err, qs, k, 1, fb)
+    torch.cuda.synchronize()
+    ah_o, er_o, q_o = np.zeros_like(r), np.zeros_like(r), q0.copy()
+    u_o, _, v_o, _ = O.lowrank_compress(r.copy(), ah_o, er_o, q_o, k, 1, fb)
+    if fb == 32:
+        live_g = np.abs(host(u).reshape(m, k)).sum(0) > 0
+        live_o = np.abs(u_o).sum(0) > 0
+    else:  # INT4: a dead column has scale 0 and zero codes
+        live_g = np.abs(O.int4_dequantize(host(u), np.ones(k, np.float32), m, k)).sum(0) > 0
+        live_o = np.abs(O.int4_dequantize(u_o, np.ones(k, np.float32), m, k)).sum(0) > 0
+    assert live_g.tolist() == [True, True, False, False], live_g
+    assert live_o.tolist() == live_g.tolist(), (live_o, live_g)
+    qg = host(qs)[0]
+    assert np.array_equal(qg[:, 2:], q0[:, 2:]), "dead columns keep their start vector"
+    assert np.array_equal(q_o[:, 2:], q0[:, 2:])
+    assert rel(qg[:, :2], q_o[:, :2]) <= 1e-5, rel(qg[:, :2], q_o[:, :2])
+    e = rel(host(ahat)[0], ah_o)
+    assert e <= (2e-4 if fb == 32 else 1e-3), e
+
+
 @pytest.mark.parametrize("fb", [4, 16, 32])
 def test_receiver_matches_sender(cf, dev, fb):
     wl = gen.Workload("lr", 192, 512, 2, 4, "bf16", True)
@@ -266,9 +307,11 @@ def test_flux_shape(cf, dev, O, rank, iters):
         prev = A
 
 
-# slots 0 and 6 each hold one INT4 code at a rounding tie at some step (see
-# explain_int4_ties); slot 7 comes closest to the bar without one
-@pytest.mark.parametrize("rank,iters,samples", [(32, 2, [0, 6, 7]), (8, 10, [0, 5])])
+# A fixed spread over the 114 tensors (first, last and two between), plus the tensors
+# that hold an INT4 code at a rounding tie at some step of this trajectory (slot 6 at
+# rank 32; explain_int4_ties accepts such a code) and the one that comes closest to the
+# bar without one (slot 7 at rank 32, slot 5 at rank 8).
+@pytest.mark.parametrize("rank,iters,samples", [(32, 2, [0, 6, 7, 37, 76, 113]), (8, 10, [0, 5, 37, 76, 113])])
 def test_flux_whole_trajectory(cf, dev, O, rank, iters, samples):
     """All 28 FLUX steps (1 warmup, 27 compressed) of 114 tensors per call with INT4
     factors and the warm-started basis carried from step to step; sampled tensors are
@@ -289,6 +332,34 @@ def test_flux_whole_trajectory(cf, dev, O, rank, iters, samples):
         A = tr.next()
         check_step(cf, dev, O, prev, A, ahat, err, qs, rank, iters, 4, samples=samples, tol=1e-3)
         prev = A
+
+
+@pytest.mark.parametrize("batch", [7, 16])
+def test_split_call_matches_one_call_per_tensor(cf, dev, batch):
+    """A call of 7 or 16 FLUX-shard tensors (22M or 50M elements) runs as two halves on two
+    streams; one call per tensor runs as a single launch sequence.  Every output of every
+    tensor (reconstruction, error, q_state, payload) is the same bit for bit."""
+    m, n, k = 1024, 3072, 32
+    wl = gen.Workload("split", m, n, batch, 2, "bf16", True)
+    tr = gen.Trajectory(wl, 17)
+    A0, A1 = (to_dev(tr.next(), dev).view(batch, m, n) for _ in range(2))
+    q0 = torch.from_numpy(start_bases(17, batch, n, k)).to(dev)
+    say(f"two-stream call of {batch} tensors against one call per tensor")
+    ah = torch.empty((batch, m, n), dtype=torch.float32, device=dev)
+    er = torch.empty_like(ah)
+    cf.init_state(A0, ah, er)
+    q = q0.clone()
+    pay = cf.lowrank_compress(A1, ah, er, q, k, 2, 4)
+    ah1 = torch.empty_like(ah)
+    er1 = torch.empty_like(ah)
+    cf.init_state(A0, ah1, er1)
+    q1 = q0.clone()
+    pays = [cf.lowrank_compress(A1[b:b + 1], ah1[b:b + 1], er1[b:b + 1], q1[b:b + 1], k, 2, 4) for b in range(batch)]
+    torch.cuda.synchronize()
+    for x, y in ((ah, ah1), (er, er1), (q, q1)):
+        assert torch.equal(x, y)
+    for i in range(4):
+        assert torch.equal(pay[i], torch.cat([p[i] for p in pays]))
 
 
 def test_deterministic(cf, dev):
