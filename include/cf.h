@@ -3,12 +3,13 @@
  * with sender-side error feedback, on MI355X (gfx950).
  *
  * Method: "Accelerating Parallel Diffusion Model Serving with Residual
- * Compression" (CompactFusion summary), section Approach: at every denoising
- * step each layer activation is sent as the compressed difference from the
- * previous *reconstructed* activation, the sender keeps error feedback so the
- * quantization error does not accumulate, and a low-rank variant with INT4
- * factors reaches extreme ratios; the measured-effects table names the
- * Compact-1bit, Compact-2bit and Compact-Lowrank variants and the warmup steps.
+ * Compression" (CompactFusion summary), section Approach; the measured-effects
+ * table names the variants built here (Compact-1bit, Compact-2bit,
+ * Compact-Lowrank) and the warmup steps.  In short: what crosses the wire at a
+ * denoising step is the residual between a layer's activation and the
+ * reconstruction both sides already hold, compressed; the sender keeps the part
+ * the compression lost and feeds it into the next step's residual; the low-rank
+ * variant sends two INT4-quantized factors instead of codes.
  *
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer on the current HIP device, allocated and
@@ -87,8 +88,8 @@ int cf_init_state(int a_dtype, const void* a, float* ahat, float* err, int64_t n
  * previous reconstruction with sender-side error feedback).  Per group g of 128
  * contiguous elements:
  *   r = a - ahat                                         (fp32)
- *   bits = 1: s = mean|r| (32 partial sums of 4 consecutive |r|, combined by the
- *             butterfly L_j += L_{j^o} for o = 16, 8, 4, 2, 1, then / 128);
+ *   bits = 1: s = mean|r| over the group, taken exactly and rounded once to
+ *             fp32 (to nearest, ties to even), so it depends on no summation order;
  *             code = (r < 0);  d = code ? -s : s
  *   bits = 2: s = max|r| / 1.5 (IEEE division);  sign = (r < 0),
  *             mag = (|r| > s);  code = sign | mag << 1;
@@ -209,10 +210,12 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
                         void* stream);
 
 /*
- * Receiver step, Compact-Lowrank: ahat = ahat + U^ V^^T for `batch` tensors, with
- * the sender's dequantization and the sender's reconstruction kernel, so the
- * receiver's ahat equals the sender's bit for bit.  Buffers and limits as in
- * cf_lowrank_compress; u, u_scales, v, v_scales in; ahat in/out.
+ * Receiver step, Compact-Lowrank (Approach: the receiver rebuilds the activation by
+ * adding the decoded low-rank residual to its copy of the previous reconstruction;
+ * measured-effects table: rank 32 with INT4 factors):  ahat = ahat + U^ V^^T for
+ * `batch` tensors, with the sender's dequantization and the sender's reconstruction
+ * kernel, so the receiver's ahat equals the sender's bit for bit.  Buffers and limits
+ * as in cf_lowrank_compress; u, u_scales, v, v_scales in; ahat in/out.
  */
 int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
                           const float* v_scales, float* ahat, int64_t m, int64_t n, int rank,
