@@ -160,13 +160,20 @@ def cpu_baseline(wl, host_steps, bits, threads):
         dt2 = time.perf_counter() - t2
         lowrank[f"r{rank}_q{iters}_int4"] = {"ms_per_tensor": round(dt2 * 1e3, 1),
                                              "GBs": round(wl.m * wl.n * 2 / dt2 / 1e9, 5)}
+    import gen as _gen
+
+    avail = _gen.affinity_cores()
     return {
         "value": round(elems * 2 / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
+        "cores_available": avail,
+        "thread_cap": None if threads == avail else
+        f"{threads} worker threads: the host CPU share of one GPU, of {avail} cores the process may use",
         "kind": "oracle",
         "sample": f"{nsteps} compressed steps x {S} tensors of {wl.m}x{wl.n} bf16 "
-                  f"(Compact-{bits}bit, one tensor per task), {dt:.2f} s wall",
+                  f"(Compact-{bits}bit, one tensor per task, {threads} threads), {dt:.2f} s wall, "
+                  f"{dt * threads:.1f} thread-seconds",
         "single_thread_GBs": round(wl.m * wl.n * 2 / dt1 / 1e9, 4),
         "lowrank_single_thread": lowrank,
     }
@@ -185,6 +192,8 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="skip the secondary rows")
     ap.add_argument("--rows", default="",
                     help="comma-separated name prefixes of the secondary rows to run (default all)")
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="whole-trajectory repeats timed after the headline steps (0: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -205,13 +214,13 @@ def main():
     wl = gen.WORKLOADS["flux"]
     numel = wl.numel
     bits = 1
-    n_gen = min(1 + args.warmup + args.steps, wl.steps)
+    n_gen = wl.steps  # the whole trajectory: the timed steps, then the repeats over all of it
     log(f"generating {n_gen} steps of {wl.slots} x {wl.m}x{wl.n} bf16 on the host")
     t0 = time.perf_counter()
     tr = gen.Trajectory(wl, args.seed)
     steps_d = []
     host_keep = []
-    n_host = 8  # steps kept on the host for the oracle baseline (7 compressed: ~16 s of CPU work)
+    n_host = 4  # steps kept on the host for the oracle baseline (3 compressed: ~25 s of CPU work)
     for t in range(n_gen):
         a = tr.next()
         if t < n_host:
@@ -282,6 +291,8 @@ def main():
     log(f"compress1 step {ms_per_step:.3f} ms, {value:.1f} GB/s act, launch {avg_launch_ms*1e3:.1f} us "
         f"-> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM), wall {wall:.3f} s")
 
+    trajectory = trajectory_repeats(torch, slab, steps_d, per_call, args.repeats) if args.repeats else None
+
     rows = {}
     if not args.no_rows:
         want = [w for w in args.rows.split(",") if w]
@@ -328,10 +339,45 @@ def main():
             "hbm_fraction_of_step": round(value * BYTES_PER_ELEM["compress1"] / 2 / HBM_PEAK_GBS, 4),
         },
         "roofline": roofline,
+        "trajectory": trajectory,
         "cpu_baseline": cpu,
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
+
+
+def _median(x):
+    x = sorted(x)
+    h = len(x) // 2
+    return x[h] if len(x) % 2 else 0.5 * (x[h - 1] + x[h])
+
+
+def trajectory_repeats(torch, slab, steps_d, per_call, repeats):
+    """The headline step over the whole trajectory, `repeats` times: warmup step 0, then
+    every compressed step once, each bracketed by events; per repeat and over all of
+    them, the mean and median step time."""
+    per_rep = []
+    for _ in range(repeats):
+        slab.init(steps_d[0], per_call)
+        torch.cuda.synchronize()
+        marks = []
+        for t in range(1, len(steps_d)):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append(e)
+            slab.compress(steps_d[t], per_call)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks.append(e)
+        torch.cuda.synchronize()
+        per_rep.append([a.elapsed_time(b) for a, b in zip(marks, marks[1:])])
+    flat = [x for r in per_rep for x in r]
+    out = {"repeats": repeats, "compressed_steps_per_repeat": len(per_rep[0]),
+           "ms_per_step_mean": round(sum(flat) / len(flat), 4), "ms_per_step_median": round(_median(flat), 4),
+           "per_repeat_mean": [round(sum(r) / len(r), 4) for r in per_rep],
+           "per_repeat_median": [round(_median(r), 4) for r in per_rep]}
+    log(f"trajectory x{repeats}: mean {out['ms_per_step_mean']} ms, median {out['ms_per_step_median']} ms per step")
+    return out
 
 
 def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want=()):
@@ -498,6 +544,36 @@ def per_layer_row(torch, cf, dev, wl, steps_d, compressed, row):
     torch.cuda.empty_cache()
 
 
+def kernel_times(torch, fn, reps=3):
+    """Device time per call of each low-rank kernel that fn() launches, from a separate
+    profiled pass of `reps` calls (torch.profiler, which on ROCm reads the kernel records
+    of the HIP runtime's tracer), in microseconds, keyed by kernel name.  None when the
+    profiler cannot record device activity here."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+
+        fn()
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for _ in range(reps):
+                fn()
+            torch.cuda.synchronize()
+        out = {}
+        for ev in prof.key_averages():
+            m = re.search(r"k_lr_([a-z]+)(ILb1E|<true)?", ev.key)
+            if not m:
+                continue
+            name = "k_lr_" + m.group(1) + ("<first>" if m.group(1) == "project" and m.group(2) else "")
+            t = getattr(ev, "device_time_total", None)
+            if t is None:
+                t = getattr(ev, "cuda_time_total", 0.0)
+            out[name] = round(out.get(name, 0.0) + t / reps, 1)
+        return out or None
+    except Exception as exc:  # noqa: BLE001 - the profiler is optional here
+        log(f"kernel_times: profiler unavailable ({type(exc).__name__}: {exc})")
+        return None
+
+
 def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on):
     """Compact-Lowrank on the FLUX shard: one call per step over all 114 tensors."""
     for rank, iters in ((32, 2), (8, 10)):
@@ -528,6 +604,14 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
                       "payload_bytes_per_tensor": wl.m * rank // 2 + wl.n * rank // 2 + 8 * rank}
         log(f"{name}: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM, "
             f"{rows[name]['tflops']} TFLOP/s")
+        kt = kernel_times(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat, err, qs, rank,
+                                                             iters, 4, pay, ws))
+        rows[name]["kernel_us_per_call"] = kt
+        if kt:
+            orth = sum(v for k, v in kt.items() if k in ("k_lr_gram", "k_lr_chol", "k_lr_solve"))
+            rows[name]["orth_us_per_call"] = round(orth, 1)
+            rows[name]["orth_us_per_iteration"] = round(orth / iters, 1)
+            log(f"{name}: kernels (us per call) {kt}; orth {orth:.1f} us per call")
         rx = torch.empty_like(ahat)
         cf.init_state(steps_d[0], rx)
         ms = time_calls(torch, lambda: cf.lowrank_decompress(4, pay, rx, rank), 4)

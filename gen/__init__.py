@@ -60,12 +60,20 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def default_threads() -> int:
+# Worker threads for host-side work: at most the CPU share one GPU's host gives a job.
+THREAD_CAP = 16
+
+
+def affinity_cores() -> int:
+    """CPU cores this process may run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def default_threads() -> int:
+    return max(1, min(affinity_cores(), THREAD_CAP))
 
 
 @dataclass(frozen=True)
