@@ -70,16 +70,16 @@ int valid_numel(int64_t numel) {
 
 int64_t act_bytes(int a_dtype, int64_t numel) { return numel * (a_dtype == CF_BF16 ? 2 : 4); }
 
-// Checks of cf_lowrank_compress.  `workspace` may be null only when `fixed_scratch` is set
-// (a buffer of the library's own, checked by the caller).
+// Checks of cf_lowrank_compress, in the order of the file header: a workspace of
+// `ws_bytes` at `workspace` (null for a buffer of the library's own, which then needs no
+// NULL or overlap check), `too_small` the status when the call needs more than ws_bytes.
 int check_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n, int rank,
                            int iters, int factor_bits, int batch, float* q_state, void* u, float* u_scales,
-                           void* v, float* v_scales, const void* workspace, bool fixed_scratch,
-                           size_t* need_out) {
+                           void* v, float* v_scales, const void* workspace, size_t ws_bytes, int too_small) {
     if (a_dtype != CF_BF16 && a_dtype != CF_F32) return CF_E_ARG;
     if (factor_bits != 4 && factor_bits != 16 && factor_bits != 32) return CF_E_ARG;
     if (iters < 1 || iters > 64) return CF_E_ARG;
-    if (!a || !ahat || !q_state || !u || !v || (!workspace && !fixed_scratch)) return CF_E_NULL;
+    if (!a || !ahat || !q_state || !u || !v || (!workspace && too_small == CF_E_WORKSPACE)) return CF_E_NULL;
     if (factor_bits == 4 && (!u_scales || !v_scales)) return CF_E_NULL;
     const size_t need = cf_lowrank_workspace_bytes(m, n, rank, batch);
     if (need == 0 || (factor_bits == 4 && (rank & 1))) return CF_E_SHAPE;
@@ -87,6 +87,7 @@ int check_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, 
         !aligned4(u) || !aligned4(v) || (u_scales && !aligned4(u_scales)) ||
         (v_scales && !aligned4(v_scales)) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return CF_E_ALIGN;
+    if (ws_bytes < need) return too_small;
     const int64_t numel = m * n * batch;
     const int64_t fsz = factor_bits / 4;  // factor bytes per (row, rank) pair, times 2
     const Range r[8] = {range_of(a, act_bytes(a_dtype, numel)),
@@ -104,7 +105,6 @@ int check_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, 
         for (const Range& x : r)
             if (x.hi > x.lo && overlap(x, wsr)) return CF_E_ALIAS;
     }
-    *need_out = need;
     return CF_OK;
 }
 
@@ -275,11 +275,9 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
                         int rank, int iters, int factor_bits, int batch, float* q_state, void* u,
                         float* u_scales, void* v, float* v_scales, void* workspace, size_t ws_bytes,
                         void* stream) {
-    size_t need = 0;
     if (int rc = check_lowrank_compress(a_dtype, a, ahat, err, m, n, rank, iters, factor_bits, batch, q_state, u,
-                                        u_scales, v, v_scales, workspace, false, &need))
+                                        u_scales, v, v_scales, workspace, ws_bytes, CF_E_WORKSPACE))
         return rc;
-    if (ws_bytes < need) return CF_E_WORKSPACE;
     if (int rc = check_device()) return rc;
     return cf::launch_lowrank_compress(a_dtype, a, ahat, err, m, n, rank, iters, factor_bits, batch,
                                        q_state, u, u_scales, v, v_scales, workspace,

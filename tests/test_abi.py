@@ -168,6 +168,9 @@ def test_lowrank_validation(L):
     assert call(a=0x100008) == CF_E_ALIGN
     assert call(w=0x1000010) == CF_E_ALIGN           # workspace is 256-byte aligned
     assert call(wsb=ws - 1) == CF_E_WORKSPACE
+    # a too-small workspace is reported as such, even where the size the call needs
+    # would run into another operand (the size check comes before the overlap check)
+    assert call(w=0x200000 - 1024, wsb=1024) == CF_E_WORKSPACE
     assert call(e=0x200000 + 64 * 128 * 4 - 16) == CF_E_ALIAS
     assert call(w=0x200000) == CF_E_ALIAS
     assert call() == CF_E_DEVICE
