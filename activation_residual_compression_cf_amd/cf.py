@@ -21,7 +21,8 @@ CF_MODE_NOEF, CF_MODE_NAIVE = 1, 2
 GROUP = 128
 
 STATUS = {0: "CF_OK", -1: "CF_E_NULL", -2: "CF_E_SHAPE", -3: "CF_E_ALIGN", -4: "CF_E_ARG",
-          -5: "CF_E_ALIAS", -6: "CF_E_WORKSPACE", -7: "CF_E_DEVICE", -8: "CF_E_HIP"}
+          -5: "CF_E_ALIAS", -6: "CF_E_WORKSPACE", -7: "CF_E_DEVICE", -8: "CF_E_HIP", -9: "CF_E_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CF_NOALLOC_SCRATCH_BYTES
 
 # name -> (restype, argtypes) ; i=int, l=int64, p=pointer, z=size_t
 _SIG = {
@@ -33,6 +34,7 @@ _SIG = {
     "cf_topk_compress": ("i", "iippppplp"),
     "cf_topk_decompress": ("i", "ippplp"),
     "cf_lowrank_compress": ("i", "ipppllii" "iipppppp" "zp"),
+    "cf_lowrank_compress_noalloc": ("i", "ipppllii" "iippppp" "p"),
     "cf_lowrank_decompress": ("i", "ipppp" "pllii" "p"),
     "cf_lowrank_workspace_bytes": ("z", "llii"),
     "cf_codes_bytes": ("l", "li"),
@@ -408,6 +410,27 @@ def lowrank_compress(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | No
         _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err), m, n, rank, iters, factor_bits, batch,
         _ptr(q_state), _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return u, us, v, vs
+
+
+def lowrank_compress_noalloc(a: torch.Tensor, ahat: torch.Tensor, err: torch.Tensor | None,
+                             q_state: torch.Tensor, rank: int, iters: int, factor_bits: int, payload,
+                             stream=None):
+    """cf_lowrank_compress_noalloc: one low-rank sender step that uses the library's fixed
+    device scratch instead of a workspace, for callers that cannot allocate.  Every buffer,
+    the payload (u, u_scales, v, v_scales) included, comes from the caller; nothing is
+    allocated here.  Calls that may overlap on one GPU race on that scratch."""
+    batch, m, n = a.shape
+    u, us, v, vs = payload
+    _check_lowrank_buffers(batch, m, n, rank, factor_bits, payload)
+    numel = batch * m * n
+    for nm, t in (("ahat", ahat), ("err", err), ("q_state", q_state)):
+        _dtype(nm, t, _F32)
+    for nm, t, nb in (("ahat", ahat, 4 * numel), ("err", err, 4 * numel), ("q_state", q_state, 4 * batch * n * rank)):
+        _need(nm, t, nb, rank >= 1)
+    _check("cf_lowrank_compress_noalloc", lib.cf_lowrank_compress_noalloc(
+        _act_dtype(a), _ptr(a), _ptr(ahat), _ptr(err), m, n, rank, iters, factor_bits, batch,
+        _ptr(q_state), _ptr(u), _ptr(us), _ptr(v), _ptr(vs), _stream(stream)))
     return u, us, v, vs
 
 

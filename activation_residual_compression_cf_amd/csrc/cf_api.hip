@@ -64,6 +64,26 @@ int check_device() {
     return g_dev_ok[dev] ? CF_OK : CF_E_DEVICE;
 }
 
+// Fixed scratch of cf_lowrank_compress_noalloc: one copy in every device's memory that
+// the library's code object is loaded on, for the life of the process.  Host code must
+// not use the array's name as an address (it names a host-side stand-in); it takes the
+// device address from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[CF_NOALLOC_SCRATCH_BYTES];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch, or nullptr when HIP refuses it.
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
 int valid_numel(int64_t numel) {
     return (numel > 0 && numel % CF_GROUP == 0 && numel <= kMaxNumel) ? CF_OK : CF_E_SHAPE;
 }
@@ -125,6 +145,9 @@ const char* cf_strerror(int status) {
         case CF_E_WORKSPACE: return "workspace missing or too small";
         case CF_E_DEVICE: return "current device is not gfx950";
         case CF_E_HIP: return "HIP runtime refused the launch";
+        case CF_E_SCRATCH:
+            return "call needs more scratch than cf_lowrank_compress_noalloc's fixed buffer "
+                   "(CF_NOALLOC_SCRATCH_BYTES) holds; pass fewer tensors per call";
         default: return "unknown status";
     }
 }
@@ -282,6 +305,22 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
     return cf::launch_lowrank_compress(a_dtype, a, ahat, err, m, n, rank, iters, factor_bits, batch,
                                        q_state, u, u_scales, v, v_scales, workspace,
                                        static_cast<hipStream_t>(stream)) == hipSuccess
+               ? CF_OK
+               : CF_E_HIP;
+}
+
+int cf_lowrank_compress_noalloc(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,
+                                int rank, int iters, int factor_bits, int batch, float* q_state, void* u,
+                                float* u_scales, void* v, float* v_scales, void* stream) {
+    if (int rc = check_lowrank_compress(a_dtype, a, ahat, err, m, n, rank, iters, factor_bits, batch, q_state, u,
+                                        u_scales, v, v_scales, nullptr, CF_NOALLOC_SCRATCH_BYTES, CF_E_SCRATCH))
+        return rc;
+    if (int rc = check_device()) return rc;
+    void* ws = scratch_for_current_device();
+    if (!ws) return CF_E_HIP;
+    return cf::launch_lowrank_compress(a_dtype, a, ahat, err, m, n, rank, iters, factor_bits, batch, q_state,
+                                       u, u_scales, v, v_scales, ws, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
                ? CF_OK
                : CF_E_HIP;
 }

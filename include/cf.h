@@ -60,9 +60,11 @@ enum {
     CF_E_ALIAS = -5,     /* an output range overlaps another operand */
     CF_E_WORKSPACE = -6, /* workspace missing or too small */
     CF_E_DEVICE = -7,    /* current device is not gfx950 */
-    CF_E_HIP = -8        /* the HIP runtime refused a launch; a call that launches several
+    CF_E_HIP = -8,       /* the HIP runtime refused a launch; a call that launches several
                             kernels (cf_lowrank_compress) may then have applied part of
                             its update, so treat the state as lost (re-run the warmup) */
+    CF_E_SCRATCH = -9    /* cf_lowrank_compress_noalloc: the call needs more scratch than
+                            the fixed CF_NOALLOC_SCRATCH_BYTES */
 };
 
 enum { CF_BF16 = 0, CF_F32 = 1 };
@@ -220,6 +222,28 @@ int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int
 int cf_lowrank_decompress(int factor_bits, const void* u, const float* u_scales, const void* v,
                           const float* v_scales, float* ahat, int64_t m, int64_t n, int rank,
                           int batch, void* stream);
+
+/*
+ * cf_lowrank_compress without a workspace argument, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Identical arguments, results and errors to
+ * cf_lowrank_compress, except that the workspace is a fixed buffer of
+ * CF_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory from the first
+ * load of its code object until the process ends; the call allocates nothing.
+ *   - A call whose cf_lowrank_workspace_bytes(m, n, rank, batch) exceeds
+ *     CF_NOALLOC_SCRATCH_BYTES returns CF_E_SCRATCH and writes nothing (64 MiB holds
+ *     four 1024 x 3072 tensors at rank 32; split larger batches into several calls).
+ *   - Every call on one GPU uses that GPU's one buffer: calls that may overlap in time
+ *     on one GPU (different streams, or several host threads) race and give wrong
+ *     results.  Order them on one stream, or use cf_lowrank_compress with a workspace
+ *     per stream.  Nothing in the buffer needs to start at zero: each call writes every
+ *     byte it reads before reading it.
+ */
+#define CF_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int cf_lowrank_compress_noalloc(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,
+                                int rank, int iters, int factor_bits, int batch, float* q_state, void* u,
+                                float* u_scales, void* v, float* v_scales, void* stream);
 
 /* Workspace bytes cf_lowrank_compress needs (0 for arguments outside the limits). */
 size_t cf_lowrank_workspace_bytes(int64_t m, int64_t n, int rank, int batch);

@@ -65,8 +65,8 @@ def test_no_torch_in_the_library():
 
 def test_strerror_and_version(lib):
     lib.cf_strerror.restype = ctypes.c_char_p
-    for code in range(0, -9, -1):
-        assert lib.cf_strerror(code) and lib.cf_strerror(code) != b"unknown status"
+    for code in range(0, -10, -1):
+        assert lib.cf_strerror(code) and lib.cf_strerror(code) != b"unknown status" and lib.cf_strerror(code) != b"unknown status"
     assert lib.cf_abi_version() == 1
 
 
@@ -186,6 +186,28 @@ def test_lowrank_validation(L):
                                    P(0x500000), 64, 128, 8, 1, None) == CF_E_ALIAS
     assert L.cf_lowrank_decompress(4, P(0x500000), P(0x600000), P(0x700000), P(0x800000),
                                    P(0x200000), 64, 128, 8, 1, None) == CF_E_DEVICE
+
+
+def test_lowrank_noalloc_validation(L):
+    """The no-allocation variant validates like cf_lowrank_compress and refuses, before
+    anything is enqueued, a call whose workspace would not fit its fixed scratch."""
+    CF_E_SCRATCH = -9
+    L.cf_lowrank_compress_noalloc.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 3 +
+                                              [ctypes.c_int64] * 2 + [ctypes.c_int] * 4 +
+                                              [ctypes.c_void_p] * 6)
+    G = 1 << 40  # placeholder buffers far apart, so no two of them overlap
+
+    def call(dt=0, m=64, n=128, k=8, it=2, fb=4, b=1, a=1 * G, us=6 * G):
+        return L.cf_lowrank_compress_noalloc(dt, P(a), P(2 * G), P(3 * G), m, n, k, it, fb, b, P(4 * G),
+                                             P(5 * G), P(us) if us else None, P(7 * G), P(8 * G), None)
+
+    assert call(fb=8) == CF_E_ARG
+    assert call(us=0) == CF_E_NULL
+    assert call(k=7) == CF_E_SHAPE
+    assert call(a=G + 8) == CF_E_ALIGN
+    assert call(m=1024, n=3072, k=32, b=5) == CF_E_SCRATCH   # 66.6 MiB of workspace
+    assert call(m=1024, n=3072, k=32, b=4) == CF_E_DEVICE    # 53.3 MiB: fits
+    assert call() == CF_E_DEVICE
 
 
 def test_ablation_and_bf16_decode_validation(L):
