@@ -194,6 +194,8 @@ def main():
                     help="comma-separated name prefixes of the secondary rows to run (default all)")
     ap.add_argument("--repeats", type=int, default=3,
                     help="whole-trajectory repeats timed after the headline steps (0: none)")
+    ap.add_argument("--no-kernel-times", action="store_true",
+                    help="skip the profiled pass that times each low-rank kernel (for runs under rocprofv3)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -296,7 +298,8 @@ def main():
     rows = {}
     if not args.no_rows:
         want = [w for w in args.rows.split(",") if w]
-        rows = secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want)
+        rows = secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want,
+                              kernel_times_on=not args.no_kernel_times)
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -380,7 +383,7 @@ def trajectory_repeats(torch, slab, steps_d, per_call, repeats):
     return out
 
 
-def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want=()):
+def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, want=(), kernel_times_on=True):
     """The other rows of the path, each timed with events over whole steps.  `want`
     selects rows by name prefix (all when empty)."""
     numel = wl.numel
@@ -405,7 +408,7 @@ def secondary_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, per_call, w
     if on("compress1_flux_per_layer"):
         per_layer_row(torch, cf, dev, wl, steps_d, compressed, row)
     if on("lowrank"):
-        lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on)
+        lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on, kernel_times_on)
     if on("topk"):
         topk_rows(torch, cf, dev, wl, steps_d, compressed, row, on)
     if on("noerr"):
@@ -574,7 +577,7 @@ def kernel_times(torch, fn, reps=3):
         return None
 
 
-def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on):
+def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_elems, on, kernel_times_on=True):
     """Compact-Lowrank on the FLUX shard: one call per step over all 114 tensors."""
     for rank, iters in ((32, 2), (8, 10)):
         if not on(f"lowrank_r{rank}_q{iters}"):
@@ -605,7 +608,7 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
         log(f"{name}: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM, "
             f"{rows[name]['tflops']} TFLOP/s")
         kt = kernel_times(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat, err, qs, rank,
-                                                             iters, 4, pay, ws))
+                                                             iters, 4, pay, ws)) if kernel_times_on else None
         rows[name]["kernel_us_per_call"] = kt
         if kt:
             orth = sum(v for k, v in kt.items() if k in ("k_lr_gram", "k_lr_chol", "k_lr_solve"))
