@@ -56,6 +56,19 @@ __device__ __forceinline__ vd4 mfma_f64(double a, double b, vd4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ vf4 ld4(const float* p) { return *reinterpret_cast<const vf4*>(p); }
+
+// r in the workspace is strip-major: per tensor, strip s holds columns 16 s .. 16 s + 15 of
+// every row, row after row (m x 16 floats, contiguous).  Every pass over r then moves 1 KB
+// runs (16 rows of one strip) per wave instruction, and the fused pass reads whole strips.
+__device__ __forceinline__ int64_t strip_off(int64_t m, int64_t row, int64_t col) {
+    return (col >> 4) * (m << 4) + (row << 4) + (col & 15);
+}
+
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding
+// (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima, no wait)
+constexpr int vm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 // Activation loads kept raw until use, so a prefetch does not wait for its data.
 template <typename ActT>
 struct RawAct;
@@ -166,7 +179,10 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
     }
 
     const int64_t rend = (rb + 1) * kProjRows < m ? (rb + 1) * kProjRows : m;
-    // staging: wave w forms rows sr + 4 w + q; lane l columns c0 + 256 h + 4 l
+    // staging.  First pass (a and Ahat, row-major): wave w forms rows sr + 4 w + q, lane l
+    // columns c0 + 256 h + 4 l.  Later passes (r, strip-major): instruction (q, h) of wave w
+    // reads strip 4 (2 q + h) + w of the segment, lane l row sr + l / 4, columns 4 (l % 4)
+    // of the strip, one 1 KB run.
     using RA = RawAct<ActT>;
     typename RA::T pa[4][2];
     vf4 ph[4][2];
@@ -175,14 +191,16 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int64_t col = c0 + 256 * h + 4 * lane;
-                const int64_t off = b * mn + (sr + 4 * wave + q) * n + col;
-                const bool ok = col < n;
                 if constexpr (FIRST) {
+                    const int64_t col = c0 + 256 * h + 4 * lane;
+                    const int64_t off = b * mn + (sr + 4 * wave + q) * n + col;
+                    const bool ok = col < n;
                     pa[q][h] = ok ? RA::load(a, off) : RA::zero();
                     ph[q][h] = ok ? ld_nt(ahat + off) : vf4{0.f, 0.f, 0.f, 0.f};
                 } else {
-                    ph[q][h] = ok ? ld_nt(r + off) : vf4{0.f, 0.f, 0.f, 0.f};
+                    const int64_t scol = c0 + 16 * (4 * (2 * q + h) + wave);
+                    ph[q][h] = scol < n ? ld_nt(r + b * mn + strip_off(m, sr + (lane >> 2), scol + 4 * (lane & 3)))
+                                        : vf4{0.f, 0.f, 0.f, 0.f};
                 }
             }
     };
@@ -193,16 +211,25 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int rr = 4 * wave + q;
-                const int cc = 256 * h + 4 * lane;
-                vf4 x = ph[q][h];
                 if constexpr (FIRST) {
-                    x = RA::cvt(pa[q][h]) - x;
-                    if (c0 + cc < n) st_nt(r + b * mn + (sr + rr) * n + c0 + cc, x);
+                    *reinterpret_cast<vf4*>(&slab[4 * wave + q][256 * h + 4 * lane]) = RA::cvt(pa[q][h]) - ph[q][h];
+                } else {
+                    const int st = 4 * (2 * q + h) + wave;
+                    *reinterpret_cast<vf4*>(&slab[lane >> 2][16 * st + 4 * (lane & 3)]) = ph[q][h];
                 }
-                *reinterpret_cast<vf4*>(&slab[rr][cc]) = x;
             }
         __syncthreads();
+        if constexpr (FIRST) {
+            // r to the workspace, strip-major: instruction i of wave w stores strip 4 i + w of
+            // the segment (its 16 rows of 16 columns, one 1 KB run)
+#pragma unroll
+            for (int i = 0; i < kSegCols / 64; ++i) {
+                const int st = 4 * i + wave;
+                if (c0 + 16 * st < n)
+                    st_nt(r + b * mn + strip_off(m, sr + (lane >> 2), c0 + 16 * st + 4 * (lane & 3)),
+                          *reinterpret_cast<const vf4*>(&slab[lane >> 2][16 * st + 4 * (lane & 3)]));
+            }
+        }
         if (sr + kStage < rend) fetch(sr + kStage);  // next stage's loads overlap the MFMAs
         vf4 acc[KT];
 #pragma unroll
@@ -470,9 +497,6 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 #pragma unroll
         for (int t = 0; t < KT; ++t) acc[i][t] = vf4{0.f, 0.f, 0.f, 0.f};
 
-    // Staging column of this lane, clamped into the tensor: a column past n loads a
-    // valid column whose products only reach output columns that are never stored.
-    const int64_t col = c0 + 4 * lane < n ? c0 + 4 * lane : n - 4;
     const int64_t nst = m / kStage;
     // Two register buffers and two LDS buffers, addressed by name (the loop is unrolled
     // by two).  While a stage's MFMAs run on one LDS buffer, the wave waits for the next
@@ -481,10 +505,16 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
     // reload the last one and are never used).
     vf4 rq[2][4];
     float pq[2][KT];
+    // r is strip-major: instruction q of wave w reads strip 4 q + w of the workgroup's 16, lane
+    // l row sr + l / 4 and columns 4 (l % 4) of the strip, one 1 KB run.  A strip past n
+    // loads a valid one, whose products only reach output columns that are never stored.
     auto fetch = [&](vf4 (&rx)[4], float (&px)[KT], int64_t st) {
         const int64_t sr = (st < nst ? st : nst - 1) * kStage;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rx[q] = ld_nt(rb + (sr + 4 * wave + q) * n + col);
+        for (int q = 0; q < 4; ++q) {
+            const int64_t scol = c0 + 16 * (4 * q + wave) < n ? c0 + 16 * (4 * q + wave) : n - 16;
+            rx[q] = ld_nt(rb + strip_off(m, sr + (lane >> 2), scol + 4 * (lane & 3)));
+        }
 #pragma unroll
         for (int j = 0; j < KT; ++j) {  // kStage * kp = 256 KT values, KT per thread
             const int e = threadIdx.x + 256 * j;
@@ -494,7 +524,7 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
     auto put = [&](float (&sl)[kStage][kBackCols + 4], float (&pp)[kStage][kp + 1], const vf4 (&rx)[4],
                    const float (&px)[KT]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&sl[4 * wave + q][4 * lane]) = rx[q];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<vf4*>(&sl[lane >> 2][16 * (4 * q + wave) + 4 * (lane & 3)]) = rx[q];
 #pragma unroll
         for (int j = 0; j < KT; ++j) {
             const int e = threadIdx.x + 256 * j;
@@ -542,6 +572,166 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
                 const vf4 o = vf4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
                 *reinterpret_cast<vf4*>(qtb + (16 * t + 4 * lg + v) * n + wc) = o;
             }
+    }
+}
+
+// ------------------------------------------------------------ fused pass ----
+// Iterations after the first: Q = r^T P (the back-projection) and the next Y = r Q (the
+// projection) in one pass over r, which the two passes would otherwise read twice.  With r
+// strip-major a strip (16 columns of one tensor over all m rows) is one contiguous block.
+// Workgroup: 8 waves over kFusedStrips consecutive strips of one tensor, moved into a
+// two-slot LDS ring by direct global-to-LDS loads (the next strip's loads are in flight
+// while the current one is used).  Row tiles of 16 rows are dealt to the waves in turn.
+// Per strip:
+//   A  Q^T[kk][c] = sum over rows of P[row][kk] r[row][c]: MFMA 16x16x4 with P^T as the A
+//      operand (in registers for the whole workgroup) and 4 rows of the strip as B; the
+//      waves' partial tiles are summed in LDS in wave order;
+//   B  Y[row][kk] += sum over the strip's columns of r[row][c] Q^T[kk][c]: a lane's float4
+//      of a row gives 4 k-slices, Q^T from LDS; the accumulators stay in registers over all
+//      of the workgroup's strips.
+// At the end each wave writes its rows of Y to Ypart[b][part] (part = the workgroup's strip
+// range), which the orthonormalisation sums in part order.  Used for m <= 1024 and padded
+// rank <= 32: the LDS then holds two strips and the reductions.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedStrips = 24;
+constexpr int kFusedMaxRows = 1024;
+
+template <int KT>
+__global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* __restrict__ r,
+                                                                   const float* __restrict__ p,
+                                                                   float* __restrict__ ypart, int64_t m, int64_t n,
+                                                                   int64_t batch, int64_t nparts, int64_t total) {
+    constexpr int kp = 16 * KT;
+    constexpr int RT = kFusedMaxRows / 16 / kFusedWaves;  // row tiles per wave, at most
+    // The two slots are separate arrays, each read and written only through its own name,
+    // so the compiler can see that reads of one do not depend on loads into the other.
+    __shared__ float slot0[kFusedMaxRows * 16];
+    __shared__ float slot1[kFusedMaxRows * 16];
+    __shared__ float red[kFusedWaves][KT][16][17];
+    __shared__ float qs[kp][20];
+    const int64_t lw = xcd_remap(blockIdx.x, total);
+    if (lw >= batch * nparts) return;  // uniform per workgroup
+    const int64_t b = lw / nparts, part = lw % nparts;
+    const int64_t s0 = part * kFusedStrips;
+    const int64_t nstrips = n >> 4;
+    const int ns = static_cast<int>(nstrips - s0 < kFusedStrips ? nstrips - s0 : kFusedStrips);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int mt = static_cast<int>(m >> 4);
+    const float* rb = r + b * m * n;
+
+    // strip j into dst: instruction i of wave w moves the float4 chunks 64 (8 i + w) .. + 63
+    // of the strip (lane l the chunk at + l) to the same place in LDS
+    const int nch = static_cast<int>(m * 4);  // float4 chunks per strip, a multiple of 64
+    auto issue = [&](int j, float* dst) __attribute__((always_inline)) {
+        const float* src = rb + (s0 + j) * (m << 4);
+#pragma unroll
+        for (int i = 0; i < kFusedMaxRows * 4 / (64 * kFusedWaves); ++i) {
+            const int c0 = 64 * (kFusedWaves * i + wave);
+            if (c0 < nch)
+                __builtin_amdgcn_global_load_lds((gvoid*)(src + 4 * (c0 + lane)), (lvoid*)(dst + 4 * c0), 16, 0, 0);
+        }
+    };
+
+    // P^T operands of phase A.  Tile jt of this wave holds rows 16 T .. 16 T + 15, T = wave + 8 jt;
+    // chunk c its rows 16 T + 4 c .. + 3; lane: P[16 T + 4 c + lg][16 t + li].
+    const float* pb = p + b * m * kp;
+    float pv[RT][4][KT];
+    vf4 acc[RT][KT];
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) {
+        const int T = wave + kFusedWaves * jt;
+#pragma unroll
+        for (int t = 0; t < KT; ++t) acc[jt][t] = vf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int t = 0; t < KT; ++t) pv[jt][c][t] = T < mt ? pb[(16 * T + 4 * c + lg) * kp + 16 * t + li] : 0.0f;
+    }
+
+    // Rows m .. kFusedMaxRows - 1 of both slots stay zero, so every wave runs all of its row
+    // tiles with no branch: tiles past m meet zero rows of r and zero rows of P and add
+    // nothing (the loads never write those rows).
+    for (int e = static_cast<int>(m) * 16 + 4 * tid; e < kFusedMaxRows * 16;
+         e += 4 * 64 * kFusedWaves) {
+        *reinterpret_cast<vf4*>(slot0 + e) = vf4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<vf4*>(slot1 + e) = vf4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // One strip held in cur.  Waits and barriers are written out: the compiler's own barrier
+    // would also wait for the next strip's loads, which are meant to stay in flight across
+    // the strip's work.
+    auto strip = [&](const float* cur) __attribute__((always_inline)) {
+        // A: this wave's partial Q^T of the strip (two accumulator sets per tile column)
+        vf4 qa[2][KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) qa[0][t] = qa[1][t] = vf4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) {
+            const int T = wave + kFusedWaves * jt;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float bv = cur[(16 * T + 4 * c + lg) * 16 + li];
+#pragma unroll
+                for (int t = 0; t < KT; ++t) qa[c & 1][t] = mfma4(pv[jt][c][t], bv, qa[c & 1][t]);
+            }
+        }
+        // qa lane: Q^T rows 16 t + 4 lg + v, strip column li
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wave][t][4 * lg + v][li] = qa[0][t][v] + qa[1][t][v];
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (tid < kp * 16) {  // the waves' partials summed in wave order
+            const int kk = tid >> 4, cc = tid & 15;
+            float q = red[0][kk >> 4][kk & 15][cc];
+#pragma unroll
+            for (int w = 1; w < kFusedWaves; ++w) q = q + red[w][kk >> 4][kk & 15][cc];
+            qs[kk][cc] = q;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // B: lane's B operand for k-slice i is Q^T[16 t + li][4 lg + i]; its A operand
+        // r[16 T + li][4 lg + i]
+        vf4 qb[KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) qb[t] = *reinterpret_cast<const vf4*>(&qs[16 * t + li][4 * lg]);
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) {
+            const int T = wave + kFusedWaves * jt;
+            const vf4 av = *reinterpret_cast<const vf4*>(&cur[(16 * T + li) * 16 + 4 * lg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int t = 0; t < KT; ++t) acc[jt][t] = mfma4(av[i], qb[t][i], acc[jt][t]);
+        }
+        // this wave's loads of the next strip have landed; after the barrier every wave's
+        // have, and every wave is done with this strip's slot, red and qs
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    issue(0, slot0);
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // strips alternate between the slots; a slot is loaded again only after the barrier
+    // that ends the strip last read from it
+    for (int j = 0; j < ns; j += 2) {
+        if (j + 1 < ns) issue(j + 1, slot1);
+        strip(slot0);
+        if (j + 1 < ns) {
+            if (j + 2 < ns) issue(j + 2, slot0);
+            strip(slot1);
+        }
+    }
+    // acc[jt][t] lane: Y rows 16 T + 4 lg + v, column 16 t + li
+    float* yp = ypart + (b * nparts + part) * m * kp;
+#pragma unroll
+    for (int jt = 0; jt < RT; ++jt) {
+        const int T = wave + kFusedWaves * jt;
+        if (T < mt)
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) yp[(16 * T + 4 * lg + v) * kp + 16 * t + li] = acc[jt][t][v];
     }
 }
 
@@ -1002,8 +1192,9 @@ int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 // share this computation.  Every workgroup has 256 threads (kCholThreads for the
 // factorisation, one workgroup per tensor).
 struct LowrankGrids {
-    int64_t kp, nseg, gblocks;
-    int64_t prep, project, gram, chol, solve, backproject, quant, reconstruct;
+    int64_t kp, nseg, nparts, gblocks;
+    int64_t prep, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
+    bool fused;  // iterations after the first run the fused pass
 };
 
 LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
@@ -1017,6 +1208,9 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
     g.chol = batch;
     g.solve = batch * ((m + 255) / 256);
     g.backproject = round8(batch * ((n + kBackCols - 1) / kBackCols));
+    g.fused = g.kp <= 32 && m <= kFusedMaxRows;
+    g.nparts = (n / 16 + kFusedStrips - 1) / kFusedStrips;
+    g.backfore = round8(batch * g.nparts);
     g.quant = batch * ((m + 255) / 256 + (n + 255) / 256);
     g.reconstruct = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
     return g;
@@ -1061,14 +1255,18 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     }
     int64_t ptotal = grid.project;
     int64_t btotal = grid.backproject;
+    int64_t ftotal = grid.backfore;
+    int64_t nparts = grid.nparts;
+    const bool fused = KT <= 2 && grid.fused;
+    void* pargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &ptotal};
+    if ((e = go(&k_lr_project<true, ActT, KT>, ptotal, pargs, stream)) != hipSuccess) return e;
+    if (after_first && (e = hipEventRecord(after_first, stream)) != hipSuccess) return e;
     for (int it = 0; it < iters; ++it) {
-        void* pargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &ptotal};
-        e = it == 0 ? go(&k_lr_project<true, ActT, KT>, ptotal, pargs, stream)
-                    : go(&k_lr_project<false, ActT, KT>, ptotal, pargs, stream);
-        if (e != hipSuccess) return e;
-        if (it == 0 && after_first && (e = hipEventRecord(after_first, stream)) != hipSuccess) return e;
+        // orth of Y: its partials come from the column segments of a projection, or from
+        // the strip ranges of a fused pass
+        int64_t parts = it > 0 && fused ? nparts : nseg;
         int64_t gblocks = grid.gblocks;
-        void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch};
+        void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &parts, &batch};
         if ((e = go(&k_lr_gram<KT>, grid.gram, gargs, stream)) != hipSuccess) return e;
         void* cargs[] = {(void*)&ws.gpart, (void*)&ws.lfac, (void*)&ws.alive, &gblocks, &k};
         if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>),
@@ -1078,7 +1276,20 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         void* sargs[] = {(void*)&ws.p, (void*)&ws.lfac, &m, &batch};
         if ((e = go(&k_lr_solve<KT>, grid.solve, sargs, stream)) != hipSuccess) return e;
         void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal};
-        if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
+        if (it + 1 == iters) {  // the last Q, the one that is sent
+            if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
+        } else if (fused) {     // Q of this iteration and Y of the next in one pass
+            if constexpr (KT <= 2) {
+                void* fargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.ypart, &m, &n, &batch, &nparts, &ftotal};
+                if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_backfore<KT>),
+                                         dim3(static_cast<unsigned>(ftotal)), dim3(64 * kFusedWaves), fargs, 0,
+                                         stream)) != hipSuccess)
+                    return e;
+            }
+        } else {
+            if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
+            if ((e = go(&k_lr_project<false, ActT, KT>, ptotal, pargs, stream)) != hipSuccess) return e;
+        }
     }
     {
         const int64_t qblocks = grid.quant;
@@ -1204,7 +1415,8 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t sz_r = up(batch * m * n * 4);
     const int64_t sz_qt = up(batch * kp * n * 4);
-    const int64_t sz_y = up(batch * nseg * m * kp * 4);
+    const LowrankGrids g = lowrank_grids(m, n, rank, batch);
+    const int64_t sz_y = up(batch * (g.fused && g.nparts > nseg ? g.nparts : nseg) * m * kp * 4);
     const int64_t sz_p = up(batch * m * kp * 4);
     const int64_t sz_al = up(batch * kp * 4);
     const int64_t sz_g = up(batch * gblocks * kp * kp * 8);
@@ -1238,7 +1450,7 @@ bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch) {
     const int64_t blocks[] = {g.prep, g.project, g.gram, g.solve, g.backproject, g.quant, g.reconstruct};
     for (int64_t b : blocks)
         if (b * 256 > kMaxDispatchItems) return false;
-    return g.chol * kCholThreads <= kMaxDispatchItems;
+    return g.chol * kCholThreads <= kMaxDispatchItems && g.backfore * 64 * kFusedWaves <= kMaxDispatchItems;
 }
 
 hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,

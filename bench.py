@@ -52,12 +52,22 @@ BYTES_PER_ELEM = {
 }
 
 
-def lowrank_bytes_per_elem(iters: int) -> float:
+def lowrank_fused(m: int, rank: int) -> bool:
+    """Whether the library runs the iterations after the first as one fused pass over r
+    (back-projection and the next projection together): for m <= 1024 rows and a rank
+    padded to 16 of at most 32.  The kernel list of a profiled call shows k_lr_backfore
+    exactly when this holds."""
+    return m <= 1024 and (rank + 15) // 16 * 16 <= 32
+
+
+def lowrank_bytes_per_elem(iters: int, fused: bool = False) -> float:
     """Algorithmic HBM bytes per element of one low-rank step: the first projection
     reads a and Ahat and writes r (10 B), each further projection and each
     back-projection reads r (4 B), the reconstruction reads a and Ahat and writes
-    Ahat and e (14 B)."""
-    return 10 + 4 * (iters - 1) + 4 * iters + 14
+    Ahat and e (14 B).  With the fused pass a back-projection and the next projection
+    read r once, so r is read iters + 1 times in all instead of 2 iters."""
+    reads = iters + 1 if fused else 2 * iters
+    return 10 + 4 * (reads - 1) + 14
 
 
 def lowrank_flops_per_elem(rank: int, iters: int) -> float:
@@ -512,7 +522,8 @@ def noerr_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, row, rows, step
     a3 = [steps_d[c].view(wl.slots, wl.m, wl.n) for c in compressed]
     ms = time_calls(torch, lambda: cf.lowrank_compress(a3[next(it) % len(a3)], ah3, None, qs, rank, iters, 4,
                                                        pay, ws), 4)
-    bpe = lowrank_bytes_per_elem(iters) - 6  # the reconstruction reads ahat only and writes ahat
+    # the reconstruction reads ahat only and writes ahat
+    bpe = lowrank_bytes_per_elem(iters, lowrank_fused(wl.m, rank)) - 6
     hbm = step_elems * bpe / (ms / 1e3) / 1e9
     rows["noerr_lowrank_r32_q2_int4_flux"] = {"ms_per_step": round(ms, 4), "hbm_GBs": round(hbm, 1),
                                                "hbm_frac": round(hbm / HBM_PEAK_GBS, 4), "bytes_per_elem": bpe}
@@ -595,7 +606,8 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
         it4 = iter(range(10 ** 9))
         ms = time_calls(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat,
                                                            err, qs, rank, iters, 4, pay, ws), 4)
-        bpe = lowrank_bytes_per_elem(iters)
+        fused = lowrank_fused(wl.m, rank)
+        bpe = lowrank_bytes_per_elem(iters, fused)
         fpe = lowrank_flops_per_elem(rank, iters)
         hbm = step_elems * bpe / (ms / 1e3) / 1e9
         name = f"lowrank_r{rank}_q{iters}_int4_flux"
@@ -603,13 +615,17 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
                       "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
                       "tflops": round(step_elems * fpe / (ms / 1e3) / 1e12, 2),
                       "mfma_fp32_frac": round(step_elems * fpe / (ms / 1e3) / 1e12 / MFMA_FP32_TFLOPS, 4),
-                      "bytes_per_elem": bpe, "flops_per_elem": fpe,
+                      "bytes_per_elem": bpe, "fused_pass": fused,
+                      "bytes_per_elem_unfused": lowrank_bytes_per_elem(iters), "flops_per_elem": fpe,
                       "payload_bytes_per_tensor": wl.m * rank // 2 + wl.n * rank // 2 + 8 * rank}
         log(f"{name}: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM, "
             f"{rows[name]['tflops']} TFLOP/s")
         kt = kernel_times(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat, err, qs, rank,
                                                              iters, 4, pay, ws)) if kernel_times_on else None
         rows[name]["kernel_us_per_call"] = kt
+        if kt and ("k_lr_backfore" in kt) != fused:
+            log(f"{name}: the profiled kernels disagree with the fused-pass rule ({sorted(kt)})")
+            rows[name]["fused_rule_mismatch"] = True
         if kt:
             orth = sum(v for k, v in kt.items() if k in ("k_lr_gram", "k_lr_chol", "k_lr_solve"))
             rows[name]["orth_us_per_call"] = round(orth, 1)
