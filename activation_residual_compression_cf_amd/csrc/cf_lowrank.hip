@@ -30,6 +30,8 @@
 //                   Gram, Cholesky with the rank guard, P = Y R^-1.
 //   k_lr_backproject Q^T = P^T r, MFMA; the four waves of a workgroup split the rows
 //                   and their partials are summed in LDS in a fixed order.
+//   k_lr_backfore   every iteration but the last, for m <= 1024 and padded rank <= 32:
+//                   Q = r^T P and the next Y = r Q in one pass over r.
 //   k_lr_colmax, k_lr_pack  INT4 (or bf16 / fp32) factors, scales, q_state update.
 //   k_lr_reconstruct Ahat += U^ V^^T (MFMA, factors dequantized on the fly from the
 //                   payload) and e = a - Ahat; the receiver runs the same kernel
@@ -66,6 +68,7 @@ __device__ __forceinline__ int64_t strip_off(int64_t m, int64_t row, int64_t col
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
+typedef float vf2 __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate that waits until at most n vector-memory loads are outstanding
 // (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima, no wait)
 constexpr int vm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -578,35 +581,42 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 // ------------------------------------------------------------ fused pass ----
 // Iterations after the first: Q = r^T P (the back-projection) and the next Y = r Q (the
 // projection) in one pass over r, which the two passes would otherwise read twice.  With r
-// strip-major a strip (16 columns of one tensor over all m rows) is one contiguous block.
-// Workgroup: 8 waves over kFusedStrips consecutive strips of one tensor, moved into a
-// two-slot LDS ring by direct global-to-LDS loads (the next strip's loads are in flight
-// while the current one is used).  Row tiles of 16 rows are dealt to the waves in turn.
-// Per strip:
+// strip-major a strip (16 columns of one tensor over all m rows) is one contiguous block,
+// and each 16 x 16 row tile of it is 1 KiB.
+// Workgroup: 8 waves over kFusedStrips consecutive strips of one tensor.  Wave w owns the
+// row tiles T = w + 8 jt (jt < RT) of every strip: it moves them into its own part of a
+// two-slot LDS ring by direct global-to-LDS loads and is the only wave that reads them, so
+// the ring needs no barrier, only each wave's own load counter.  Per strip:
 //   A  Q^T[kk][c] = sum over rows of P[row][kk] r[row][c]: MFMA 16x16x4 with P^T as the A
-//      operand (in registers for the whole workgroup) and 4 rows of the strip as B; the
-//      waves' partial tiles are summed in LDS in wave order;
+//      operand (in registers for the whole workgroup) and 4 rows of a tile as B.  The same
+//      pass copies each tile in row layout into registers for B, after which the slot is
+//      free and the wave starts the loads of the strip after next into it, so two strips
+//      are in flight while B runs;
+//   the waves' partial Q^T tiles are summed in LDS in wave order (two barriers);
 //   B  Y[row][kk] += sum over the strip's columns of r[row][c] Q^T[kk][c]: a lane's float4
 //      of a row gives 4 k-slices, Q^T from LDS; the accumulators stay in registers over all
 //      of the workgroup's strips.
 // At the end each wave writes its rows of Y to Ypart[b][part] (part = the workgroup's strip
 // range), which the orthonormalisation sums in part order.  Used for m <= 1024 and padded
-// rank <= 32: the LDS then holds two strips and the reductions.
+// rank <= 32; RT = 2, 4 or 8 tiles per wave covers m <= 256, 512 or 1024.  Tiles past the
+// last row tile of the tensor re-read that tile: their P rows are zero, so they add exact
+// zeros to Q^T, and their Y rows are not stored.
 constexpr int kFusedWaves = 8;
 constexpr int kFusedStrips = 24;
 constexpr int kFusedMaxRows = 1024;
 
-template <int KT>
+template <int KT, int RT>
 __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* __restrict__ r,
                                                                    const float* __restrict__ p,
                                                                    float* __restrict__ ypart, int64_t m, int64_t n,
                                                                    int64_t batch, int64_t nparts, int64_t total) {
     constexpr int kp = 16 * KT;
-    constexpr int RT = kFusedMaxRows / 16 / kFusedWaves;  // row tiles per wave, at most
+    constexpr int kTile = 256;  // floats of one 16 x 16 tile
     // The two slots are separate arrays, each read and written only through its own name,
     // so the compiler can see that reads of one do not depend on loads into the other.
-    __shared__ float slot0[kFusedMaxRows * 16];
-    __shared__ float slot1[kFusedMaxRows * 16];
+    // Wave w's tile jt sits at (w RT + jt) kTile in either slot.
+    __shared__ float slot0[kFusedWaves * RT * kTile];
+    __shared__ float slot1[kFusedWaves * RT * kTile];
     __shared__ float red[kFusedWaves][KT][16][17];
     __shared__ float qs[kp][20];
     const int64_t lw = xcd_remap(blockIdx.x, total);
@@ -617,23 +627,28 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
     const int ns = static_cast<int>(nstrips - s0 < kFusedStrips ? nstrips - s0 : kFusedStrips);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
     const int mt = static_cast<int>(m >> 4);
-    const float* rb = r + b * m * n;
+    const float* rs = r + b * m * n + s0 * (m << 4);  // the range's first strip
 
-    // strip j into dst: instruction i of wave w moves the float4 chunks 64 (8 i + w) .. + 63
-    // of the strip (lane l the chunk at + l) to the same place in LDS
-    const int nch = static_cast<int>(m * 4);  // float4 chunks per strip, a multiple of 64
-    auto issue = [&](int j, float* dst) __attribute__((always_inline)) {
-        const float* src = rb + (s0 + j) * (m << 4);
+    // this lane's 16 bytes of tile jt inside a strip
+    int toff[RT];
 #pragma unroll
-        for (int i = 0; i < kFusedMaxRows * 4 / (64 * kFusedWaves); ++i) {
-            const int c0 = 64 * (kFusedWaves * i + wave);
-            if (c0 < nch)
-                __builtin_amdgcn_global_load_lds((gvoid*)(src + 4 * (c0 + lane)), (lvoid*)(dst + 4 * c0), 16, 0, 0);
-        }
+    for (int jt = 0; jt < RT; ++jt) {
+        const int T = wave + kFusedWaves * jt;
+        toff[jt] = (T < mt ? T : mt - 1) * kTile + 4 * lane;
+    }
+    // Strips past the range reload its last strip (from L2) into a slot that is no longer
+    // read: every strip then has the same loads in flight behind it, so one wait count
+    // serves every strip, and the compiler, which sees the same pattern on every path,
+    // adds no wait of its own before the reads of a slot.
+    auto issue = [&](int j, float* dst) __attribute__((always_inline)) {
+        const float* src = rs + (j < ns ? j : ns - 1) * (m << 4);
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt)
+            __builtin_amdgcn_global_load_lds((gvoid*)(src + toff[jt]), (lvoid*)(dst + (wave * RT + jt) * kTile), 16,
+                                             0, 0);
     };
 
-    // P^T operands of phase A.  Tile jt of this wave holds rows 16 T .. 16 T + 15, T = wave + 8 jt;
-    // chunk c its rows 16 T + 4 c .. + 3; lane: P[16 T + 4 c + lg][16 t + li].
+    // P^T operands of A.  Lane: P[16 T + 4 c + lg][16 t + li] for tile jt, chunk c.
     const float* pb = p + b * m * kp;
     float pv[RT][4][KT];
     vf4 acc[RT][KT];
@@ -647,34 +662,48 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
 #pragma unroll
             for (int t = 0; t < KT; ++t) pv[jt][c][t] = T < mt ? pb[(16 * T + 4 * c + lg) * kp + 16 * t + li] : 0.0f;
     }
+    // after the P loads, so that the first strip's wait below covers them too
+    issue(0, slot0);
+    issue(1, slot1);
+    __builtin_amdgcn_s_waitcnt(vm_wait(RT));  // strip 0 has landed; strip 1 may not have
 
-    // Rows m .. kFusedMaxRows - 1 of both slots stay zero, so every wave runs all of its row
-    // tiles with no branch: tiles past m meet zero rows of r and zero rows of P and add
-    // nothing (the loads never write those rows).
-    for (int e = static_cast<int>(m) * 16 + 4 * tid; e < kFusedMaxRows * 16;
-         e += 4 * 64 * kFusedWaves) {
-        *reinterpret_cast<vf4*>(slot0 + e) = vf4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<vf4*>(slot1 + e) = vf4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // One strip held in cur.  Waits and barriers are written out: the compiler's own barrier
-    // would also wait for the next strip's loads, which are meant to stay in flight across
-    // the strip's work.
-    auto strip = [&](const float* cur) __attribute__((always_inline)) {
-        // A: this wave's partial Q^T of the strip (two accumulator sets per tile column)
+    // Strip j, held in cur.  The waits and barriers are written out: the compiler's own
+    // barrier would also wait for the loads of the next strips, which stay in flight.
+    auto strip = [&](int j, float* cur) __attribute__((always_inline)) {
+        // (this wave's loads of strip j have landed: the wait ends the previous strip)
+        const float* wt = cur + wave * RT * kTile;
         vf4 qa[2][KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) qa[0][t] = qa[1][t] = vf4{0.f, 0.f, 0.f, 0.f};
+        vf4 rv[RT];  // B operands: rv[jt] = r[16 T + li][4 lg .. 4 lg + 3] of the strip
+        // The slot is read with the wait written into the same statement: read through the
+        // array, the compiler waits for the loads into the other slot as well (it cannot
+        // tell them apart on every path), which would leave one strip in flight instead of
+        // two.  Per tile: the A-side values of chunks 0..3 (rows 4 c + lg, column li; 256
+        // bytes apart) and the row-layout float4.
+        const unsigned wa = static_cast<unsigned>(reinterpret_cast<size_t>((lvoid*)wt));
 #pragma unroll
         for (int jt = 0; jt < RT; ++jt) {
-            const int T = wave + kFusedWaves * jt;
+            vf2 b01, b23;
+            asm volatile(
+                "ds_read2st64_b32 %0, %3 offset1:1\n\t"
+                "ds_read2st64_b32 %1, %3 offset0:2 offset1:3\n\t"
+                "ds_read_b128 %2, %4\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(b01), "=&v"(b23), "=&v"(rv[jt])
+                : "v"(wa + jt * 1024 + 4 * lane), "v"(wa + jt * 1024 + 64 * li + 16 * lg)
+                : "memory");
+            const float bvs[4] = {b01[0], b01[1], b23[0], b23[1]};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float bv = cur[(16 * T + 4 * c + lg) * 16 + li];
+                const float bv = bvs[c];
 #pragma unroll
                 for (int t = 0; t < KT; ++t) qa[c & 1][t] = mfma4(pv[jt][c][t], bv, qa[c & 1][t]);
             }
         }
+        // every read of the slot by this wave has returned: refill it with strip j + 2
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(j + 2, cur);
         // qa lane: Q^T rows 16 t + 4 lg + v, strip column li
 #pragma unroll
         for (int t = 0; t < KT; ++t)
@@ -682,46 +711,60 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
             for (int v = 0; v < 4; ++v) red[wave][t][4 * lg + v][li] = qa[0][t][v] + qa[1][t][v];
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         if (tid < kp * 16) {  // the waves' partials summed in wave order
+            // The eight reads are written out with their wait: read through the array, the
+            // compiler would first wait for every load in flight into the ring, which cannot
+            // write red.
+            static_assert(kFusedWaves == 8, "one read per wave below");
             const int kk = tid >> 4, cc = tid & 15;
-            float q = red[0][kk >> 4][kk & 15][cc];
-#pragma unroll
-            for (int w = 1; w < kFusedWaves; ++w) q = q + red[w][kk >> 4][kk & 15][cc];
-            qs[kk][cc] = q;
+            const unsigned ad = static_cast<unsigned>(reinterpret_cast<size_t>((lvoid*)&red[0][kk >> 4][kk & 15][cc]));
+            constexpr int wb = KT * 16 * 17 * 4;  // bytes from one wave's partials to the next
+            float v0, v1, v2, v3, v4, v5, v6, v7;
+            asm volatile(
+                "ds_read_b32 %0, %8\n\t"
+                "ds_read_b32 %1, %8 offset:%9\n\t"
+                "ds_read_b32 %2, %8 offset:%10\n\t"
+                "ds_read_b32 %3, %8 offset:%11\n\t"
+                "ds_read_b32 %4, %8 offset:%12\n\t"
+                "ds_read_b32 %5, %8 offset:%13\n\t"
+                "ds_read_b32 %6, %8 offset:%14\n\t"
+                "ds_read_b32 %7, %8 offset:%15\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
+                : "v"(ad), "i"(wb), "i"(2 * wb), "i"(3 * wb), "i"(4 * wb), "i"(5 * wb), "i"(6 * wb), "i"(7 * wb)
+                : "memory");
+            qs[kk][cc] = ((((((v0 + v1) + v2) + v3) + v4) + v5) + v6) + v7;
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // B: lane's B operand for k-slice i is Q^T[16 t + li][4 lg + i]; its A operand
-        // r[16 T + li][4 lg + i]
+        // B: lane's B operand for k-slice i is Q^T[16 t + li][4 lg + i]
         vf4 qb[KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) qb[t] = *reinterpret_cast<const vf4*>(&qs[16 * t + li][4 * lg]);
 #pragma unroll
-        for (int jt = 0; jt < RT; ++jt) {
-            const int T = wave + kFusedWaves * jt;
-            const vf4 av = *reinterpret_cast<const vf4*>(&cur[(16 * T + li) * 16 + 4 * lg]);
+        for (int jt = 0; jt < RT; ++jt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int t = 0; t < KT; ++t) acc[jt][t] = mfma4(av[i], qb[t][i], acc[jt][t]);
-        }
-        // this wave's loads of the next strip have landed; after the barrier every wave's
-        // have, and every wave is done with this strip's slot, red and qs
-        __builtin_amdgcn_s_waitcnt(vm_wait(0));
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                for (int t = 0; t < KT; ++t) acc[jt][t] = mfma4(rv[jt][i], qb[t][i], acc[jt][t]);
+        // The next write of qs follows the first barrier of the next strip, which every wave
+        // reaches only after these reads; red likewise.  Strip j + 1 has landed once only the
+        // loads of strip j + 2 may be in flight.  (Waiting here rather than at the top of the
+        // next strip is the same point in time, and it leaves the compiler, which merges the
+        // states of all paths into a loop's first block, nothing to wait for there.)
+        // The scheduling barrier keeps B's MFMAs ahead of the wait.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vm_wait(RT));
     };
 
-    issue(0, slot0);
-    __builtin_amdgcn_s_waitcnt(vm_wait(0));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // strips alternate between the slots; a slot is loaded again only after the barrier
-    // that ends the strip last read from it
-    for (int j = 0; j < ns; j += 2) {
-        if (j + 1 < ns) issue(j + 1, slot1);
-        strip(slot0);
-        if (j + 1 < ns) {
-            if (j + 2 < ns) issue(j + 2, slot0);
-            strip(slot1);
-        }
+    // Pairs of strips, then an odd last one: every path into the loop's first block comes
+    // through a strip in slot1, so only loads into slot1 can be in flight there.
+    int j = 0;
+    for (; j + 1 < ns; j += 2) {
+        strip(j, slot0);
+        strip(j + 1, slot1);
     }
+    if (j < ns) strip(j, slot0);
+    // no load may still be writing this workgroup's LDS when it ends
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
     // acc[jt][t] lane: Y rows 16 T + 4 lg + v, column 16 t + li
     float* yp = ypart + (b * nparts + part) * m * kp;
 #pragma unroll
@@ -1281,8 +1324,10 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         } else if (fused) {     // Q of this iteration and Y of the next in one pass
             if constexpr (KT <= 2) {
                 void* fargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.ypart, &m, &n, &batch, &nparts, &ftotal};
-                if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_backfore<KT>),
-                                         dim3(static_cast<unsigned>(ftotal)), dim3(64 * kFusedWaves), fargs, 0,
+                const void* fk = m <= 256   ? reinterpret_cast<const void*>(&k_lr_backfore<KT, 2>)
+                                 : m <= 512 ? reinterpret_cast<const void*>(&k_lr_backfore<KT, 4>)
+                                            : reinterpret_cast<const void*>(&k_lr_backfore<KT, 8>);
+                if ((e = hipLaunchKernel(fk, dim3(static_cast<unsigned>(ftotal)), dim3(64 * kFusedWaves), fargs, 0,
                                          stream)) != hipSuccess)
                     return e;
             }
