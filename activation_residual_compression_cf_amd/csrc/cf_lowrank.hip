@@ -45,7 +45,11 @@ namespace cf {
 namespace {
 
 constexpr int kSegCols = 512;   // columns per projection segment
-constexpr int kProjRows = 256;  // rows per projection workgroup (16 stages of 16)
+// Rows per projection workgroup: the first pass streams a and Ahat and writes r, and it
+// runs fastest in short workgroups (4 stages of 16 rows); the re-projection re-reads its
+// Q operands from L2 at every workgroup's start and keeps 16 stages.
+template <bool FIRST>
+constexpr int proj_rows() { return FIRST ? 64 : 256; }
 constexpr int kBackCols = 256;  // columns per back-projection workgroup
 constexpr int kRecRows = 32;    // reconstruction workgroup: 32 rows x 256 columns
 constexpr int kRecCols = 256;
@@ -141,10 +145,10 @@ __global__ __launch_bounds__(256) void k_lr_prep(const float* __restrict__ q_sta
 }
 
 // ------------------------------------------------------------- project ----
-// Workgroup: 4 waves over columns [c0, c0 + 512) and rows [r0, r0 + 256), in
-// stages of 16 rows.  Wave w owns columns c0 + 128 w .. + 127 and keeps the matching
-// Q^T float4 operands (8 column groups x KT tiles) in registers for the whole
-// kernel.  Per stage the 16 x 512 slab of r is formed (first pass: a - Ahat, also
+// Workgroup: 4 waves over columns [c0, c0 + 512) and rows [r0, r0 + proj_rows) (64 rows
+// in the first pass, 256 after), in stages of 16 rows.  Wave w owns columns
+// c0 + 128 w .. + 127 and keeps the matching Q^T float4 operands (8 column groups x KT
+// tiles) in registers for the whole kernel.  Per stage the 16 x 512 slab of r is formed (first pass: a - Ahat, also
 // stored to the workspace) or read, one instruction per 256 consecutive columns
 // of a row, and staged in LDS; each wave multiplies its 128 columns (MFMA, a lane's
 // float4 of r supplying 4 k-slices), the four partial Y tiles are summed in LDS in
@@ -159,6 +163,7 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
     __shared__ float slab[kStage][kSegCols + 4];
     __shared__ float red[4][kStage][kp + 1];
     const int64_t lw = xcd_remap(blockIdx.x, total);
+    constexpr int kProjRows = proj_rows<FIRST>();
     const int64_t rblocks = (m + kProjRows - 1) / kProjRows;
     if (lw >= batch * rblocks * nseg) return;  // uniform per workgroup
     const int64_t b = lw / (rblocks * nseg);
@@ -1236,7 +1241,7 @@ int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 // factorisation, one workgroup per tensor).
 struct LowrankGrids {
     int64_t kp, nseg, nparts, gblocks;
-    int64_t prep, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
+    int64_t prep, project_first, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
     bool fused;  // iterations after the first run the fused pass
 };
 
@@ -1246,7 +1251,8 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
     g.nseg = (n + kSegCols - 1) / kSegCols;
     g.gblocks = (m + gram_rows(g.kp / 16) - 1) / gram_rows(g.kp / 16);
     g.prep = batch * ((n + 255) / 256);
-    g.project = round8(batch * ((m + kProjRows - 1) / kProjRows) * g.nseg);
+    g.project_first = round8(batch * ((m + proj_rows<true>() - 1) / proj_rows<true>()) * g.nseg);
+    g.project = round8(batch * ((m + proj_rows<false>() - 1) / proj_rows<false>()) * g.nseg);
     g.gram = batch * g.gblocks;
     g.chol = batch;
     g.solve = batch * ((m + 255) / 256);
@@ -1301,8 +1307,10 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     int64_t ftotal = grid.backfore;
     int64_t nparts = grid.nparts;
     const bool fused = KT <= 2 && grid.fused;
+    int64_t pftotal = grid.project_first;
+    void* pfargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &pftotal};
+    if ((e = go(&k_lr_project<true, ActT, KT>, pftotal, pfargs, stream)) != hipSuccess) return e;
     void* pargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &ptotal};
-    if ((e = go(&k_lr_project<true, ActT, KT>, ptotal, pargs, stream)) != hipSuccess) return e;
     if (after_first && (e = hipEventRecord(after_first, stream)) != hipSuccess) return e;
     for (int it = 0; it < iters; ++it) {
         // orth of Y: its partials come from the column segments of a projection, or from
@@ -1492,7 +1500,8 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
 
 bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch) {
     const LowrankGrids g = lowrank_grids(m, n, rank, batch);
-    const int64_t blocks[] = {g.prep, g.project, g.gram, g.solve, g.backproject, g.quant, g.reconstruct};
+    const int64_t blocks[] = {g.prep, g.project_first, g.project, g.gram, g.solve, g.backproject, g.quant,
+                              g.reconstruct};
     for (int64_t b : blocks)
         if (b * 256 > kMaxDispatchItems) return false;
     return g.chol * kCholThreads <= kMaxDispatchItems && g.backfore * 64 * kFusedWaves <= kMaxDispatchItems;
