@@ -105,9 +105,9 @@ def counter_traffic():
     return float(b.group(1))
 
 
-def time_calls(torch, fn, reps, warm=1):
-    """Mean ms per call of fn() over reps calls, each bracketed by events, after `warm`
-    untimed calls (the first launch of a kernel also loads its code object)."""
+def call_times(torch, fn, reps, warm=1):
+    """ms of each of reps back-to-back calls of fn(), each bracketed by events, after
+    `warm` untimed calls (the first launch of a kernel also loads its code object)."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
@@ -120,7 +120,13 @@ def time_calls(torch, fn, reps, warm=1):
         b.record()
         pairs.append((a, b))
     torch.cuda.synchronize()
-    return sum(x.elapsed_time(y) for x, y in pairs) / reps
+    return [x.elapsed_time(y) for x, y in pairs]
+
+
+def time_calls(torch, fn, reps, warm=1):
+    """Mean ms per call of fn() over reps back-to-back calls."""
+    ts = call_times(torch, fn, reps, warm)
+    return sum(ts) / len(ts)
 
 
 def cpu_baseline(wl, host_steps, bits, threads):
@@ -604,21 +610,23 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
         a3 = [steps_d[c].view(wl.slots, wl.m, wl.n) for c in compressed]
         cf.lowrank_compress(a3[0], ahat, err, qs, rank, iters, 4, pay, ws)
         it4 = iter(range(10 ** 9))
-        ms = time_calls(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat,
-                                                           err, qs, rank, iters, 4, pay, ws), 4)
+        ts = call_times(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat,
+                                                           err, qs, rank, iters, 4, pay, ws), 8)
+        ms = sum(ts) / len(ts)
         fused = lowrank_fused(wl.m, rank)
         bpe = lowrank_bytes_per_elem(iters, fused)
         fpe = lowrank_flops_per_elem(rank, iters)
         hbm = step_elems * bpe / (ms / 1e3) / 1e9
         name = f"lowrank_r{rank}_q{iters}_int4_flux"
-        rows[name] = {"ms_per_step": round(ms, 4), "act_GBs": round(step_elems * 2 / (ms / 1e3) / 1e9, 1),
+        rows[name] = {"ms_per_step": round(ms, 4), "ms_per_step_median": round(_median(ts), 4),
+                      "act_GBs": round(step_elems * 2 / (ms / 1e3) / 1e9, 1),
                       "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4),
                       "tflops": round(step_elems * fpe / (ms / 1e3) / 1e12, 2),
                       "mfma_fp32_frac": round(step_elems * fpe / (ms / 1e3) / 1e12 / MFMA_FP32_TFLOPS, 4),
                       "bytes_per_elem": bpe, "fused_pass": fused,
                       "bytes_per_elem_unfused": lowrank_bytes_per_elem(iters), "flops_per_elem": fpe,
                       "payload_bytes_per_tensor": wl.m * rank // 2 + wl.n * rank // 2 + 8 * rank}
-        log(f"{name}: {ms:.3f} ms/step, {hbm / HBM_PEAK_GBS:.1%} of HBM, "
+        log(f"{name}: {ms:.3f} ms/step (median {_median(ts):.3f}), {hbm / HBM_PEAK_GBS:.1%} of HBM, "
             f"{rows[name]['tflops']} TFLOP/s")
         kt = kernel_times(torch, lambda: cf.lowrank_compress(a3[1 + next(it4) % (len(a3) - 1)], ahat, err, qs, rank,
                                                              iters, 4, pay, ws)) if kernel_times_on else None
