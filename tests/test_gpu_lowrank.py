@@ -129,6 +129,31 @@ def test_step_parity_extreme_shapes(cf, dev, O, m, n, rank, iters, fb):
         prev = A
 
 
+@pytest.mark.parametrize("m,n,rank,iters,fb", [(384, 400, 16, 3, 4), (496, 16, 8, 3, 32),
+                                              (768, 784, 32, 2, 4), (240, 1552, 24, 4, 16)])
+def test_step_parity_fused_pass_shapes(cf, dev, O, m, n, rank, iters, fb):
+    """The pass that runs a back-projection and the next projection together (m <= 1024,
+    rank <= 32, two or more iterations) at each of its row-tile counts per wave (2, 4, 8
+    for m <= 256, 512, 1024), with row tiles past the tensor's last one, an odd number of
+    16-column strips in a range, a range of one strip, and a tensor of one strip; 2
+    tensors per call, 2 steps."""
+    wl = gen.Workload("lrf", m, n, 2, 3, "bf16", True)
+    say(f"lowrank fused-pass shape: {m}x{n} rank={rank} iters={iters} fb={fb}")
+    tr = gen.Trajectory(wl, 4)
+    A0 = tr.next()
+    a0 = to_dev(A0, dev)
+    ahat = torch.empty((2, m, n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(a0, ahat, err)
+    qs = torch.from_numpy(start_bases(4, 2, n, rank)).to(dev)
+    prev = A0
+    for t in range(1, 3):
+        A = tr.next()
+        check_step(cf, dev, O, prev, A, ahat, err, qs, rank, iters, fb, samples=[0, 1],
+                   tol=2e-4 if fb == 32 else 1e-3)
+        prev = A
+
+
 def test_int4_stage_isolated(cf, dev, O):
     """The INT4 codes and scales equal the oracle's quantizer on the GPU's fp32 factors."""
     wl = gen.Workload("lr", 256, 768, 2, 2, "bf16", True)
