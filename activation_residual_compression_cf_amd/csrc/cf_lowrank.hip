@@ -588,7 +588,7 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 // projection) in one pass over r, which the two passes would otherwise read twice.  With r
 // strip-major a strip (16 columns of one tensor over all m rows) is one contiguous block,
 // and each 16 x 16 row tile of it is 1 KiB.
-// Workgroup: 8 waves over kFusedStrips consecutive strips of one tensor.  Wave w owns the
+// Workgroup: 8 waves over fused_strips(KT) consecutive strips of one tensor.  Wave w owns the
 // row tiles T = w + 8 jt (jt < RT) of every strip: it moves them into its own part of a
 // two-slot LDS ring by direct global-to-LDS loads and is the only wave that reads them, so
 // the ring needs no barrier, only each wave's own load counter.  Per strip:
@@ -607,7 +607,10 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 // last row tile of the tensor re-read that tile: their P rows are zero, so they add exact
 // zeros to Q^T, and their Y rows are not stored.
 constexpr int kFusedWaves = 8;
-constexpr int kFusedStrips = 24;
+// Strips per workgroup: at rank <= 16 a workgroup takes 48 strips (fewer Y partials for the
+// orthonormalisation to read back, which pays at many iterations); at rank 17..32, whose
+// passes are longer, 24 strips leave a shorter last round of workgroups.
+constexpr int fused_strips(int64_t kt) { return kt == 1 ? 48 : 24; }
 constexpr int kFusedMaxRows = 1024;
 
 template <int KT, int RT>
@@ -627,9 +630,10 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
     const int64_t lw = xcd_remap(blockIdx.x, total);
     if (lw >= batch * nparts) return;  // uniform per workgroup
     const int64_t b = lw / nparts, part = lw % nparts;
-    const int64_t s0 = part * kFusedStrips;
+    constexpr int kStrips = fused_strips(KT);
+    const int64_t s0 = part * kStrips;
     const int64_t nstrips = n >> 4;
-    const int ns = static_cast<int>(nstrips - s0 < kFusedStrips ? nstrips - s0 : kFusedStrips);
+    const int ns = static_cast<int>(nstrips - s0 < kStrips ? nstrips - s0 : kStrips);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
     const int mt = static_cast<int>(m >> 4);
     const float* rs = r + b * m * n + s0 * (m << 4);  // the range's first strip
@@ -1258,7 +1262,7 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
     g.solve = batch * ((m + 255) / 256);
     g.backproject = round8(batch * ((n + kBackCols - 1) / kBackCols));
     g.fused = g.kp <= 32 && m <= kFusedMaxRows;
-    g.nparts = (n / 16 + kFusedStrips - 1) / kFusedStrips;
+    g.nparts = (n / 16 + fused_strips(g.kp / 16) - 1) / fused_strips(g.kp / 16);
     g.backfore = round8(batch * g.nparts);
     g.quant = batch * ((m + 255) / 256 + (n + 255) / 256);
     g.reconstruct = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
