@@ -70,12 +70,6 @@ __device__ __forceinline__ int64_t strip_off(int64_t m, int64_t row, int64_t col
     return (col >> 4) * (m << 4) + (row << 4) + (col & 15);
 }
 
-typedef __attribute__((address_space(1))) void gvoid;
-typedef __attribute__((address_space(3))) void lvoid;
-typedef float vf2 __attribute__((ext_vector_type(2)));
-// s_waitcnt immediate that waits until at most n vector-memory loads are outstanding
-// (vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima, no wait)
-constexpr int vm_wait(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 // Activation loads kept raw until use, so a prefetch does not wait for its data.
 template <typename ActT>
 struct RawAct;
@@ -589,14 +583,12 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 // strip-major a strip (16 columns of one tensor over all m rows) is one contiguous block,
 // and each 16 x 16 row tile of it is 1 KiB.
 // Workgroup: 8 waves over fused_strips(KT) consecutive strips of one tensor.  Wave w owns the
-// row tiles T = w + 8 jt (jt < RT) of every strip: it moves them into its own part of a
-// two-slot LDS ring by direct global-to-LDS loads and is the only wave that reads them, so
-// the ring needs no barrier, only each wave's own load counter.  Per strip:
+// row tiles T = w + 8 jt (jt < RT) of every strip: it loads them (one 1 KiB run per
+// instruction) into registers a strip ahead, copies them into its own part of the LDS slot
+// once it is done with the strip before, and is the only wave that reads them, so the slot
+// needs no barrier.  Per strip:
 //   A  Q^T[kk][c] = sum over rows of P[row][kk] r[row][c]: MFMA 16x16x4 with P^T as the A
-//      operand (in registers for the whole workgroup) and 4 rows of a tile as B.  The same
-//      pass copies each tile in row layout into registers for B, after which the slot is
-//      free and the wave starts the loads of the strip after next into it, so two strips
-//      are in flight while B runs;
+//      operand (in registers for the whole workgroup) and 4 rows of a tile as B;
 //   the waves' partial Q^T tiles are summed in LDS in wave order (two barriers);
 //   B  Y[row][kk] += sum over the strip's columns of r[row][c] Q^T[kk][c]: a lane's float4
 //      of a row gives 4 k-slices, Q^T from LDS; the accumulators stay in registers over all
@@ -620,11 +612,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
                                                                    int64_t batch, int64_t nparts, int64_t total) {
     constexpr int kp = 16 * KT;
     constexpr int kTile = 256;  // floats of one 16 x 16 tile
-    // The two slots are separate arrays, each read and written only through its own name,
-    // so the compiler can see that reads of one do not depend on loads into the other.
-    // Wave w's tile jt sits at (w RT + jt) kTile in either slot.
-    __shared__ float slot0[kFusedWaves * RT * kTile];
-    __shared__ float slot1[kFusedWaves * RT * kTile];
+    __shared__ float slot[kFusedWaves * RT * kTile];  // wave w's tile jt at (w RT + jt) kTile
     __shared__ float red[kFusedWaves][KT][16][17];
     __shared__ float qs[kp][20];
     const int64_t lw = xcd_remap(blockIdx.x, total);
@@ -645,16 +633,18 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
         const int T = wave + kFusedWaves * jt;
         toff[jt] = (T < mt ? T : mt - 1) * kTile + 4 * lane;
     }
-    // Strips past the range reload its last strip (from L2) into a slot that is no longer
-    // read: every strip then has the same loads in flight behind it, so one wait count
-    // serves every strip, and the compiler, which sees the same pattern on every path,
-    // adds no wait of its own before the reads of a slot.
-    auto issue = [&](int j, float* dst) __attribute__((always_inline)) {
+    // Strip j into the registers (past the range: its last strip again, whose copy is never
+    // used), and the registers into this wave's part of the slot.
+    vf4 stage[RT];
+    auto fetch = [&](int j) __attribute__((always_inline)) {
         const float* src = rs + (j < ns ? j : ns - 1) * (m << 4);
 #pragma unroll
-        for (int jt = 0; jt < RT; ++jt)
-            __builtin_amdgcn_global_load_lds((gvoid*)(src + toff[jt]), (lvoid*)(dst + (wave * RT + jt) * kTile), 16,
-                                             0, 0);
+        for (int jt = 0; jt < RT; ++jt) stage[jt] = ld_nt(src + toff[jt]);
+    };
+    float* ws = slot + wave * RT * kTile;
+    auto put = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) *reinterpret_cast<vf4*>(ws + jt * kTile + 4 * lane) = stage[jt];
     };
 
     // P^T operands of A.  Lane: P[16 T + 4 c + lg][16 t + li] for tile jt, chunk c.
@@ -671,109 +661,56 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
 #pragma unroll
             for (int t = 0; t < KT; ++t) pv[jt][c][t] = T < mt ? pb[(16 * T + 4 * c + lg) * kp + 16 * t + li] : 0.0f;
     }
-    // after the P loads, so that the first strip's wait below covers them too
-    issue(0, slot0);
-    issue(1, slot1);
-    __builtin_amdgcn_s_waitcnt(vm_wait(RT));  // strip 0 has landed; strip 1 may not have
-
-    // Strip j, held in cur.  The waits and barriers are written out: the compiler's own
-    // barrier would also wait for the loads of the next strips, which stay in flight.
-    auto strip = [&](int j, float* cur) __attribute__((always_inline)) {
-        // (this wave's loads of strip j have landed: the wait ends the previous strip)
-        const float* wt = cur + wave * RT * kTile;
+    fetch(0);
+    put();
+    fetch(1);
+    for (int j = 0; j < ns; ++j) {
+        // A: this wave's partial Q^T of the strip (two accumulator sets per tile column)
         vf4 qa[2][KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) qa[0][t] = qa[1][t] = vf4{0.f, 0.f, 0.f, 0.f};
-        vf4 rv[RT];  // B operands: rv[jt] = r[16 T + li][4 lg .. 4 lg + 3] of the strip
-        // The slot is read with the wait written into the same statement: read through the
-        // array, the compiler waits for the loads into the other slot as well (it cannot
-        // tell them apart on every path), which would leave one strip in flight instead of
-        // two.  Per tile: the A-side values of chunks 0..3 (rows 4 c + lg, column li; 256
-        // bytes apart) and the row-layout float4.
-        const unsigned wa = static_cast<unsigned>(reinterpret_cast<size_t>((lvoid*)wt));
 #pragma unroll
         for (int jt = 0; jt < RT; ++jt) {
-            vf2 b01, b23;
-            asm volatile(
-                "ds_read2st64_b32 %0, %3 offset1:1\n\t"
-                "ds_read2st64_b32 %1, %3 offset0:2 offset1:3\n\t"
-                "ds_read_b128 %2, %4\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(b01), "=&v"(b23), "=&v"(rv[jt])
-                : "v"(wa + jt * 1024 + 4 * lane), "v"(wa + jt * 1024 + 64 * li + 16 * lg)
-                : "memory");
-            const float bvs[4] = {b01[0], b01[1], b23[0], b23[1]};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float bv = bvs[c];
+                const float bv = ws[jt * kTile + (4 * c + lg) * 16 + li];
 #pragma unroll
                 for (int t = 0; t < KT; ++t) qa[c & 1][t] = mfma4(pv[jt][c][t], bv, qa[c & 1][t]);
             }
         }
-        // every read of the slot by this wave has returned: refill it with strip j + 2
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue(j + 2, cur);
         // qa lane: Q^T rows 16 t + 4 lg + v, strip column li
 #pragma unroll
         for (int t = 0; t < KT; ++t)
 #pragma unroll
             for (int v = 0; v < 4; ++v) red[wave][t][4 * lg + v][li] = qa[0][t][v] + qa[1][t][v];
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __syncthreads();
         if (tid < kp * 16) {  // the waves' partials summed in wave order
-            // The eight reads are written out with their wait: read through the array, the
-            // compiler would first wait for every load in flight into the ring, which cannot
-            // write red.
-            static_assert(kFusedWaves == 8, "one read per wave below");
             const int kk = tid >> 4, cc = tid & 15;
-            const unsigned ad = static_cast<unsigned>(reinterpret_cast<size_t>((lvoid*)&red[0][kk >> 4][kk & 15][cc]));
-            constexpr int wb = KT * 16 * 17 * 4;  // bytes from one wave's partials to the next
-            float v0, v1, v2, v3, v4, v5, v6, v7;
-            asm volatile(
-                "ds_read_b32 %0, %8\n\t"
-                "ds_read_b32 %1, %8 offset:%9\n\t"
-                "ds_read_b32 %2, %8 offset:%10\n\t"
-                "ds_read_b32 %3, %8 offset:%11\n\t"
-                "ds_read_b32 %4, %8 offset:%12\n\t"
-                "ds_read_b32 %5, %8 offset:%13\n\t"
-                "ds_read_b32 %6, %8 offset:%14\n\t"
-                "ds_read_b32 %7, %8 offset:%15\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(v4), "=&v"(v5), "=&v"(v6), "=&v"(v7)
-                : "v"(ad), "i"(wb), "i"(2 * wb), "i"(3 * wb), "i"(4 * wb), "i"(5 * wb), "i"(6 * wb), "i"(7 * wb)
-                : "memory");
-            qs[kk][cc] = ((((((v0 + v1) + v2) + v3) + v4) + v5) + v6) + v7;
+            float q = red[0][kk >> 4][kk & 15][cc];
+#pragma unroll
+            for (int w = 1; w < kFusedWaves; ++w) q = q + red[w][kk >> 4][kk & 15][cc];
+            qs[kk][cc] = q;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // B: lane's B operand for k-slice i is Q^T[16 t + li][4 lg + i]
+        __syncthreads();
+        // B: lane's B operand for k-slice i is Q^T[16 t + li][4 lg + i]; its A operand
+        // r[16 T + li][4 lg + i]
         vf4 qb[KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) qb[t] = *reinterpret_cast<const vf4*>(&qs[16 * t + li][4 * lg]);
 #pragma unroll
-        for (int jt = 0; jt < RT; ++jt)
+        for (int jt = 0; jt < RT; ++jt) {
+            const vf4 rv = *reinterpret_cast<const vf4*>(ws + jt * kTile + li * 16 + 4 * lg);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int t = 0; t < KT; ++t) acc[jt][t] = mfma4(rv[jt][i], qb[t][i], acc[jt][t]);
-        // The next write of qs follows the first barrier of the next strip, which every wave
-        // reaches only after these reads; red likewise.  Strip j + 1 has landed once only the
-        // loads of strip j + 2 may be in flight.  (Waiting here rather than at the top of the
-        // next strip is the same point in time, and it leaves the compiler, which merges the
-        // states of all paths into a loop's first block, nothing to wait for there.)
-        // The scheduling barrier keeps B's MFMAs ahead of the wait.
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(vm_wait(RT));
-    };
-
-    // Pairs of strips, then an odd last one: every path into the loop's first block comes
-    // through a strip in slot1, so only loads into slot1 can be in flight there.
-    int j = 0;
-    for (; j + 1 < ns; j += 2) {
-        strip(j, slot0);
-        strip(j + 1, slot1);
+                for (int t = 0; t < KT; ++t) acc[jt][t] = mfma4(rv[i], qb[t][i], acc[jt][t]);
+        }
+        // The wave is done with its part of the slot: strip j + 1 goes in, and the loads of
+        // strip j + 2 start.  (The next writes of red and qs follow the next strip's barriers,
+        // which every wave reaches only after its reads of them above.)
+        put();
+        fetch(j + 2);
     }
-    if (j < ns) strip(j, slot0);
-    // no load may still be writing this workgroup's LDS when it ends
-    __builtin_amdgcn_s_waitcnt(vm_wait(0));
     // acc[jt][t] lane: Y rows 16 T + 4 lg + v, column 16 t + li
     float* yp = ypart + (b * nparts + part) * m * kp;
 #pragma unroll
