@@ -635,16 +635,18 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
     }
     // Strip j into the registers (past the range: its last strip again, whose copy is never
     // used), and the registers into this wave's part of the slot.
-    vf4 stage[RT];
-    auto fetch = [&](int j) __attribute__((always_inline)) {
+    // Strips loaded ahead: two at rank <= 16, one at rank 17..32 (whose registers are full).
+    constexpr int kDepth = KT == 1 ? 2 : 1;
+    vf4 stage[kDepth][RT];
+    auto fetch = [&](int j, vf4 (&st)[RT]) __attribute__((always_inline)) {
         const float* src = rs + (j < ns ? j : ns - 1) * (m << 4);
 #pragma unroll
-        for (int jt = 0; jt < RT; ++jt) stage[jt] = ld_nt(src + toff[jt]);
+        for (int jt = 0; jt < RT; ++jt) st[jt] = ld_nt(src + toff[jt]);
     };
     float* ws = slot + wave * RT * kTile;
-    auto put = [&]() __attribute__((always_inline)) {
+    auto put = [&](const vf4 (&st)[RT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int jt = 0; jt < RT; ++jt) *reinterpret_cast<vf4*>(ws + jt * kTile + 4 * lane) = stage[jt];
+        for (int jt = 0; jt < RT; ++jt) *reinterpret_cast<vf4*>(ws + jt * kTile + 4 * lane) = st[jt];
     };
 
     // P^T operands of A.  Lane: P[16 T + 4 c + lg][16 t + li] for tile jt, chunk c.
@@ -661,10 +663,11 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
 #pragma unroll
             for (int t = 0; t < KT; ++t) pv[jt][c][t] = T < mt ? pb[(16 * T + 4 * c + lg) * kp + 16 * t + li] : 0.0f;
     }
-    fetch(0);
-    put();
-    fetch(1);
-    for (int j = 0; j < ns; ++j) {
+    fetch(0, stage[0]);
+    put(stage[0]);
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) fetch(1 + d, stage[d]);
+    auto strip = [&](int j, vf4 (&st)[RT]) __attribute__((always_inline)) {
         // A: this wave's partial Q^T of the strip (two accumulator sets per tile column)
         vf4 qa[2][KT];
 #pragma unroll
@@ -708,8 +711,18 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
         // The wave is done with its part of the slot: strip j + 1 goes in, and the loads of
         // strip j + 2 start.  (The next writes of red and qs follow the next strip's barriers,
         // which every wave reaches only after its reads of them above.)
-        put();
-        fetch(j + 2);
+        put(st);
+        fetch(j + 1 + kDepth, st);
+    };
+    if constexpr (kDepth == 2) {
+        int j = 0;
+        for (; j + 1 < ns; j += 2) {
+            strip(j, stage[0]);
+            strip(j + 1, stage[1]);
+        }
+        if (j < ns) strip(j, stage[0]);
+    } else {
+        for (int j = 0; j < ns; ++j) strip(j, stage[0]);
     }
     // acc[jt][t] lane: Y rows 16 T + 4 lg + v, column 16 t + li
     float* yp = ypart + (b * nparts + part) * m * kp;
