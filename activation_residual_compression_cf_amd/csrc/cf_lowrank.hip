@@ -633,13 +633,14 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
         const int T = wave + kFusedWaves * jt;
         toff[jt] = (T < mt ? T : mt - 1) * kTile + 4 * lane;
     }
-    // Strip j into the registers (past the range: its last strip again, whose copy is never
-    // used), and the registers into this wave's part of the slot.
-    // Strips loaded ahead: two at rank <= 16, one at rank 17..32 (whose registers are full).
+    // Strip j into the registers (nothing past the range: the copy of such a strip is never
+    // read), and the registers into this wave's part of the slot.  Strips loaded ahead: two
+    // at rank <= 16, one at rank 17..32 (whose registers are full).
     constexpr int kDepth = KT == 1 ? 2 : 1;
     vf4 stage[kDepth][RT];
     auto fetch = [&](int j, vf4 (&st)[RT]) __attribute__((always_inline)) {
-        const float* src = rs + (j < ns ? j : ns - 1) * (m << 4);
+        if (j >= ns) return;  // uniform per workgroup
+        const float* src = rs + j * (m << 4);
 #pragma unroll
         for (int jt = 0; jt < RT; ++jt) st[jt] = ld_nt(src + toff[jt]);
     };
