@@ -22,17 +22,18 @@
 // is zero and its start vector is kept in q_state.
 //
 // Kernels (each launch covers every tensor of the batch):
-//   k_lr_prep       q_state -> Q^T (rank padded to a multiple of 16 with zeros)
 //   k_lr_project    Y partials = r Q over column segments; the first pass also forms
-//                   and stores r.  fp32 MFMA 16x16x4: a lane's float4 of r supplies
+//                   and stores r, and reads Q from q_state (rank padded to a multiple of
+//                   16 with zeros).  fp32 MFMA 16x16x4: a lane's float4 of r supplies
 //                   4 k-slices, Q^T float4s the matching B operands.
 //   k_lr_gram, k_lr_chol, k_lr_solve  orth: Y = sum of partials (fixed order), fp64
-//                   Gram, Cholesky with the rank guard, P = Y R^-1.
-//   k_lr_backproject Q^T = P^T r, MFMA; the four waves of a workgroup split the rows
-//                   and their partials are summed in LDS in a fixed order.
+//                   Gram, Cholesky with the rank guard, P = Y R^-1; the last solve also
+//                   writes U's column maxima for the quantizer.
+//   k_lr_backproject Q^T = P^T r, MFMA; each wave of a workgroup owns 64 of its 256
+//                   columns over every row; the last one also writes V's column maxima.
 //   k_lr_backfore   every iteration but the last, for m <= 1024 and padded rank <= 32:
 //                   Q = r^T P and the next Y = r Q in one pass over r.
-//   k_lr_colmax, k_lr_pack  INT4 (or bf16 / fp32) factors, scales, q_state update.
+//   k_lr_pack       INT4 (or bf16 / fp32) factors, scales, q_state update.
 //   k_lr_reconstruct Ahat += U^ V^^T (MFMA, factors dequantized on the fly from the
 //                   payload) and e = a - Ahat; the receiver runs the same kernel
 //                   without e, so both sides produce identical bits.
@@ -101,43 +102,6 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t total) {
     return (w & 7) * (total >> 3) + (w >> 3);
 }
 
-// ---------------------------------------------------------------- prep ----
-// q_state (n x k per tensor, row-major) -> Q^T (kp x n, rank padded with zero rows).
-// Workgroup: 256 consecutive rows of one tensor's q_state, one contiguous span read
-// with coalesced loads into LDS, then written out one rank index at a time (256
-// consecutive floats of Q^T each).
-template <int KT>
-__global__ __launch_bounds__(256) void k_lr_prep(const float* __restrict__ q_state, float* __restrict__ qt,
-                                                  int64_t n, int k, int64_t batch) {
-    constexpr int kp = 16 * KT;
-    __shared__ float tile[256][kp + 1];
-    const int t = threadIdx.x;
-    const int64_t nb = (n + 255) / 256;
-    const int64_t b = blockIdx.x / nb;
-    const int64_t c0 = (blockIdx.x % nb) * 256;
-    const int nc = static_cast<int>(n - c0 < 256 ? n - c0 : 256);
-    const float* src = q_state + (b * n + c0) * k;  // nc rows of k floats
-    const int cnt = nc * k;
-    if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(q_state) & 15) == 0) {
-        for (int e = 4 * t; e < cnt; e += 1024) {
-            const vf4 v = ld4(src + e);
-            const int r = e / k, c = e % k;
-            tile[r][c] = v[0];
-            tile[r][c + 1] = v[1];
-            tile[r][c + 2] = v[2];
-            tile[r][c + 3] = v[3];
-        }
-    } else {
-        for (int e = t; e < cnt; e += 256) tile[e / k][e % k] = src[e];
-    }
-    __syncthreads();
-    if (t < nc) {
-        float* dst = qt + b * kp * n + c0 + t;
-#pragma unroll
-        for (int kk = 0; kk < kp; ++kk) dst[kk * n] = kk < k ? tile[t][kk] : 0.0f;
-    }
-}
-
 // ------------------------------------------------------------- project ----
 // Workgroup: 4 waves over columns [c0, c0 + 512) and rows [r0, r0 + proj_rows) (64 rows
 // in the first pass, 256 after), in stages of 16 rows.  Wave w owns columns
@@ -147,11 +111,13 @@ __global__ __launch_bounds__(256) void k_lr_prep(const float* __restrict__ q_sta
 // of a row, and staged in LDS; each wave multiplies its 128 columns (MFMA, a lane's
 // float4 of r supplying 4 k-slices), the four partial Y tiles are summed in LDS in
 // wave order, and the 16 x kp result goes to Ypart[b][segment][row][kp].
+// The first pass takes its Q operands from q_state itself (n x k per tensor, row-major;
+// rank indices k .. kp - 1 read as 0), later passes from Q^T (kp x n) in the workspace.
 template <bool FIRST, typename ActT, int KT>
 __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, const float* __restrict__ ahat,
                                                      float* __restrict__ r, const float* __restrict__ qt,
                                                      float* __restrict__ ypart, int64_t m, int64_t n,
-                                                     int64_t batch, int64_t nseg, int64_t total) {
+                                                     int64_t batch, int64_t nseg, int64_t total, int k) {
     constexpr int kp = 16 * KT;
     constexpr int kStage = 16;
     __shared__ float slab[kStage][kSegCols + 4];
@@ -170,14 +136,29 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
 
     // Q^T operands: column group g covers columns c0 + 128 w + 16 g .. + 15;
     // lane: Q^T[16 t + li][c0 + 128 w + 16 g + 4 lg .. + 3].
-    const float* qtb = qt + b * kp * n;
     vf4 qv[8][KT];
+    if constexpr (FIRST) {
+        const float* qsb = qt + b * n * k;  // q_state
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        const int64_t col = c0 + 128 * wave + 16 * g + 4 * lg;
+        for (int g = 0; g < 8; ++g) {
+            const int64_t col = c0 + 128 * wave + 16 * g + 4 * lg;
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-            qv[g][t] = col < n ? ld4(qtb + (16 * t + li) * n + col) : vf4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < KT; ++t) {
+                const int kk = 16 * t + li;
+                const bool ok = col < n && kk < k;  // n is a multiple of 16: col .. col + 3 < n
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qv[g][t][i] = ok ? qsb[(col + i) * k + kk] : 0.0f;
+            }
+        }
+    } else {
+        const float* qtb = qt + b * kp * n;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const int64_t col = c0 + 128 * wave + 16 * g + 4 * lg;
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+                qv[g][t] = col < n ? ld4(qtb + (16 * t + li) * n + col) : vf4{0.f, 0.f, 0.f, 0.f};
+        }
     }
 
     const int64_t rend = (rb + 1) * kProjRows < m ? (rb + 1) * kProjRows : m;
@@ -437,35 +418,59 @@ __global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restri
 // = 0 and zeros below it in L, so its p_j is 0 and it feeds nothing later.  The factor
 // is staged in LDS by one cooperative load; every lane then reads the same address
 // (a broadcast).
+// In the last iteration (cmax not null) the workgroup also writes the INT4 quantizer's
+// column maxima of its 256 rows of P = U: cmax[b][block][kk] = max |P[row][kk]| (rows
+// past m count as 0), nblk the blocks of U and V per tensor.
 template <int KT>
 __global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const double* __restrict__ lfac,
-                                                   int64_t m, int64_t batch) {
+                                                   int64_t m, int64_t batch, float* __restrict__ cmax,
+                                                   int64_t nblk) {
     constexpr int kp = 16 * KT;
     __shared__ double lb[kp * kp];
+    __shared__ float cm[4][kp];
     const int64_t rblocks = (m + 255) / 256;
     const int64_t b = blockIdx.x / rblocks;
-    const int64_t row = (blockIdx.x % rblocks) * 256 + threadIdx.x;
+    const int64_t blk = blockIdx.x % rblocks;
+    const int64_t row = blk * 256 + threadIdx.x;
     for (int e = threadIdx.x; e < kp * kp; e += 256) lb[e] = lfac[b * kp * kp + e];
     __syncthreads();
-    if (row >= m) return;
-    float* pr = p + (b * m + row) * kp;
-    double x[kp];
+    const bool in = row < m;
+    float pf[kp];
+    if (in) {
+        float* pr = p + (b * m + row) * kp;
+        double x[kp];
 #pragma unroll
-    for (int i = 0; i < kp; i += 4) {
-        const vf4 v = ld4(pr + i);
-        x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
+        for (int i = 0; i < kp; i += 4) {
+            const vf4 v = ld4(pr + i);
+            x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
+        }
+#pragma unroll
+        for (int j = 0; j < kp; ++j) {
+            double acc = x[j];
+#pragma unroll
+            for (int i = 0; i < j; ++i) acc = fma(-lb[j * kp + i], x[i], acc);
+            x[j] = acc * lb[j * kp + j];
+        }
+#pragma unroll
+        for (int j = 0; j < kp; ++j) pf[j] = static_cast<float>(x[j]);
+#pragma unroll
+        for (int j = 0; j < kp; j += 4) *reinterpret_cast<vf4*>(pr + j) = vf4{pf[j], pf[j + 1], pf[j + 2], pf[j + 3]};
     }
+    if (cmax) {  // uniform per launch
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < kp; ++j) {
-        double acc = x[j];
+        for (int kk = 0; kk < kp; ++kk) {
+            float v = in ? fabsf(pf[kk]) : 0.0f;
 #pragma unroll
-        for (int i = 0; i < j; ++i) acc = fma(-lb[j * kp + i], x[i], acc);
-        x[j] = acc * lb[j * kp + j];
+            for (int mask = 32; mask >= 1; mask >>= 1) v = fmaxf(v, __shfl_xor(v, mask, 64));
+            if (lane == 0) cm[wave][kk] = v;
+        }
+        __syncthreads();
+        if (threadIdx.x < kp) {
+            const int kk = threadIdx.x;
+            cmax[(b * nblk + blk) * kp + kk] = fmaxf(fmaxf(cm[0][kk], cm[1][kk]), fmaxf(cm[2][kk], cm[3][kk]));
+        }
     }
-#pragma unroll
-    for (int j = 0; j < kp; j += 4)
-        *reinterpret_cast<vf4*>(pr + j) = vf4{static_cast<float>(x[j]), static_cast<float>(x[j + 1]),
-                                              static_cast<float>(x[j + 2]), static_cast<float>(x[j + 3])};
 }
 
 // ---------------------------------------------------------- backproject ----
@@ -474,10 +479,14 @@ __global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const d
 // block of P are staged in LDS; wave w owns columns c0 + 64 w .. + 63 and
 // accumulates Q^T[kk][col] = sum_rows P[row][kk] r[row][col] with MFMA (4 rows per
 // k-slice; a lane's float4 of r gives 4 column sets).  No cross-wave reduction.
+// In the last iteration (cmax not null) the workgroup also writes the INT4 quantizer's
+// column maxima of its 256 rows of Q = V: cmax[b][mb + block][kk] = max over its columns
+// of |Q^T[kk][col]|, nblk the blocks of U and V per tensor, mb those of U.
 template <int KT>
 __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const float* p,
                                                          float* __restrict__ qt, int64_t m, int64_t n,
-                                                         int64_t batch, int64_t total) {
+                                                         int64_t batch, int64_t total, float* __restrict__ cmax,
+                                                         int64_t nblk, int64_t mb) {
     constexpr int kp = 16 * KT;
     constexpr int kStage = 16;
     __shared__ float slab[2][kStage][kBackCols + 4];
@@ -574,6 +583,28 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
                 const vf4 o = vf4{acc[0][t][v], acc[1][t][v], acc[2][t][v], acc[3][t][v]};
                 *reinterpret_cast<vf4*>(qtb + (16 * t + 4 * lg + v) * n + wc) = o;
             }
+    }
+    if (cmax) {  // uniform per launch
+        // per row kk: this lane's 4 columns (none past n), then the 16 lanes of the row
+        // group (lane bits 0..3), then the 4 waves
+        __shared__ float cm[4][kp];
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float x = wc < n ? fmaxf(fmaxf(fabsf(acc[0][t][v]), fabsf(acc[1][t][v])),
+                                         fmaxf(fabsf(acc[2][t][v]), fabsf(acc[3][t][v])))
+                                 : 0.0f;
+#pragma unroll
+                for (int mask = 8; mask >= 1; mask >>= 1) x = fmaxf(x, __shfl_xor(x, mask, 64));
+                if (li == 0) cm[wave][16 * t + 4 * lg + v] = x;
+            }
+        __syncthreads();
+        if (threadIdx.x < kp) {
+            const int kk = threadIdx.x;
+            cmax[(b * nblk + mb + c0 / 256) * kp + kk] =
+                fmaxf(fmaxf(cm[0][kk], cm[1][kk]), fmaxf(cm[2][kk], cm[3][kk]));
+        }
     }
 }
 
@@ -742,7 +773,7 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
 // Factor f of tensor b: f = 0 is U = P (m rows, row-major m x kp), f = 1 is V = Q
 // (n rows, stored transposed as Q^T kp x n).  Row blocks of 256 rows: blocks
 // [0, mb) cover U, [mb, mb + nb) cover V, for each tensor.
-// k_lr_colmax: per block and column, max |x| over the block's rows.
+// The last solve (U) and back-projection (V) leave max |x| per block and column in cmax.
 // k_lr_pack:   s = (max over the factor's blocks) / 7; one row per thread:
 //              c = rint(x / s) clamped to [-7, 7] (0 if s = 0), nibbles packed low
 //              first along the rank index (or the fp32 factor copied); V's rows
@@ -769,36 +800,6 @@ __device__ __forceinline__ void stage_factor_block(const float* x, int f, int64_
             blk[r][c + 2] = v[2];
             blk[r][c + 3] = v[3];
         }
-    }
-}
-
-template <int KT>
-__global__ __launch_bounds__(256) void k_lr_colmax(const float* __restrict__ p, const float* __restrict__ qt,
-                                                    float* __restrict__ cmax, int64_t m, int64_t n) {
-    constexpr int kp = 16 * KT;
-    constexpr int TPC = 256 / kp;  // threads per column
-    __shared__ float blk[256][kp + 1];
-    __shared__ float part[kp][TPC + 1];
-    const int64_t mb = (m + 255) / 256, nb = (n + 255) / 256;
-    const int64_t b = blockIdx.x / (mb + nb);
-    const int64_t bi = blockIdx.x % (mb + nb);
-    const int f = bi >= mb;
-    const int64_t r0 = (f ? bi - mb : bi) * 256;
-    const int64_t rows = f ? n : m;
-    const int nr = static_cast<int>(rows - r0 < 256 ? rows - r0 : 256);
-    stage_factor_block<kp>(f ? qt + b * kp * n : p + b * m * kp, f, n, r0, nr, blk);
-    __syncthreads();
-    // thread t: column t % kp over rows t / kp, t / kp + TPC, ...  (max is exact, so
-    // the order does not matter)
-    const int kk = threadIdx.x % kp, slot = threadIdx.x / kp;
-    float mx = 0.0f;
-    for (int r = slot; r < 256; r += TPC) mx = fmaxf(mx, fabsf(blk[r][kk]));
-    part[kk][slot] = mx;
-    __syncthreads();
-    if (threadIdx.x < kp) {
-        float mm = part[threadIdx.x][0];
-        for (int q = 1; q < TPC; ++q) mm = fmaxf(mm, part[threadIdx.x][q]);
-        cmax[blockIdx.x * kp + threadIdx.x] = mm;
     }
 }
 
@@ -1196,7 +1197,7 @@ int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 // factorisation, one workgroup per tensor).
 struct LowrankGrids {
     int64_t kp, nseg, nparts, gblocks;
-    int64_t prep, project_first, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
+    int64_t project_first, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
     bool fused;  // iterations after the first run the fused pass
 };
 
@@ -1205,7 +1206,6 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
     g.kp = (rank + 15) / 16 * 16;
     g.nseg = (n + kSegCols - 1) / kSegCols;
     g.gblocks = (m + gram_rows(g.kp / 16) - 1) / gram_rows(g.kp / 16);
-    g.prep = batch * ((n + 255) / 256);
     g.project_first = round8(batch * ((m + proj_rows<true>() - 1) / proj_rows<true>()) * g.nseg);
     g.project = round8(batch * ((m + proj_rows<false>() - 1) / proj_rows<false>()) * g.nseg);
     g.gram = batch * g.gblocks;
@@ -1253,19 +1253,17 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     const LowrankGrids grid = lowrank_grids(m, n, k, batch);
     int64_t nseg = grid.nseg;
     hipError_t e;
-    {
-        void* args[] = {&q_state, (void*)&ws.qt, &n, &k, &batch};
-        if ((e = go(&k_lr_prep<KT>, grid.prep, args, stream)) != hipSuccess) return e;
-    }
     int64_t ptotal = grid.project;
     int64_t btotal = grid.backproject;
     int64_t ftotal = grid.backfore;
+    int64_t mblk = (m + 255) / 256;               // U blocks of the quantizer per tensor
+    int64_t nblk = mblk + (n + 255) / 256;        // U and V blocks
     int64_t nparts = grid.nparts;
     const bool fused = KT <= 2 && grid.fused;
     int64_t pftotal = grid.project_first;
-    void* pfargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &pftotal};
+    void* pfargs[] = {&a, &ahat, (void*)&ws.r, (void*)&q_state, (void*)&ws.ypart, &m, &n, &batch, &nseg, &pftotal, &k};
     if ((e = go(&k_lr_project<true, ActT, KT>, pftotal, pfargs, stream)) != hipSuccess) return e;
-    void* pargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &ptotal};
+    void* pargs[] = {&a, &ahat, (void*)&ws.r, (void*)&ws.qt, (void*)&ws.ypart, &m, &n, &batch, &nseg, &ptotal, &k};
     if (after_first && (e = hipEventRecord(after_first, stream)) != hipSuccess) return e;
     for (int it = 0; it < iters; ++it) {
         // orth of Y: its partials come from the column segments of a projection, or from
@@ -1279,9 +1277,12 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
                                  dim3(static_cast<unsigned>(grid.chol)), dim3(kCholThreads), cargs, 0,
                                  stream)) != hipSuccess)
             return e;
-        void* sargs[] = {(void*)&ws.p, (void*)&ws.lfac, &m, &batch};
+        // the last iteration's solve and back-projection also leave the quantizer's
+        // column maxima of U and V in cmax
+        float* cmax = it + 1 == iters ? ws.cmax : nullptr;
+        void* sargs[] = {(void*)&ws.p, (void*)&ws.lfac, &m, &batch, (void*)&cmax, &nblk};
         if ((e = go(&k_lr_solve<KT>, grid.solve, sargs, stream)) != hipSuccess) return e;
-        void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal};
+        void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal, (void*)&cmax, &nblk, &mblk};
         if (it + 1 == iters) {  // the last Q, the one that is sent
             if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
         } else if (fused) {     // Q of this iteration and Y of the next in one pass
@@ -1301,8 +1302,6 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     }
     {
         const int64_t qblocks = grid.quant;
-        void* margs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.cmax, &m, &n};
-        if ((e = go(&k_lr_colmax<KT>, qblocks, margs, stream)) != hipSuccess) return e;
         void* qargs[] = {(void*)&ws.p, (void*)&ws.qt, (void*)&ws.cmax, (void*)&ws.alive, &m, &n, &k,
                          &factor_bits, &q_state, &u, &u_scales, &v, &v_scales};
         if ((e = go(&k_lr_pack<KT>, qblocks, qargs, stream)) != hipSuccess) return e;
@@ -1455,7 +1454,7 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
 
 bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch) {
     const LowrankGrids g = lowrank_grids(m, n, rank, batch);
-    const int64_t blocks[] = {g.prep, g.project_first, g.project, g.gram, g.solve, g.backproject, g.quant,
+    const int64_t blocks[] = {g.project_first, g.project, g.gram, g.solve, g.backproject, g.quant,
                               g.reconstruct};
     for (int64_t b : blocks)
         if (b * 256 > kMaxDispatchItems) return false;
