@@ -184,7 +184,12 @@ def test_random_lowrank_case(cf, dev, O, seed):
             hu, hv = m * rank // 2, n * rank // 2
             gpu_pay = (u[s * hu:(s + 1) * hu], us[s * rank:(s + 1) * rank],
                        v[s * hv:(s + 1) * hv], vs[s * rank:(s + 1) * rank])
-            flips, e = explain_int4_ties(O, np.ascontiguousarray(a[s]), ahat0[s], q0[s], rank, iters,
-                                         gpu_pay, r_gpu, tol)
-            say(f"  tensor {s}: {flips} INT4 codes at rounding ties; with them rel = {e:.2e}")
+            # the same batch from the same state with fp32 factors: the same launches and factors
+            f32 = cf.lowrank_compress(a_d, to_dev(ahat0, dev), torch.empty_like(ah_d), to_dev(q0, dev), rank,
+                                      iters, 32)
+            torch.cuda.synchronize()
+            gpu_f32 = (host(f32[0]).reshape(batch, m, rank)[s], host(f32[2]).reshape(batch, n, rank)[s])
+            flips, d, e = explain_int4_ties(O, np.ascontiguousarray(a[s]), ahat0[s], q0[s], rank, iters,
+                                            gpu_pay, gpu_f32, r_gpu, cold=True)
+            say(f"  tensor {s}: {flips} INT4 codes at rounding ties (factors within {d:.2e}); with them rel = {e:.2e}")
         assert e <= tol, f"tensor {s}: reconstruction update differs by {e:.3e}"
