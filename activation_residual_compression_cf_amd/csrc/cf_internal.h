@@ -34,20 +34,22 @@ hipError_t launch_topk_decompress(int k, const uint8_t* idx, const uint16_t* val
 struct LowrankWorkspace {
     float* r;      // batch x m x n residual
     float* qt;     // batch x kp x n, Q transposed (rank padded to a multiple of 16)
-    float* ypart;  // batch x segments x m x kp projection partials
+    float* ypart;  // Y partials: batch x segments x m x kp of a projection, or two per strip
+                   // range of a fused pass
     float* p;      // batch x m x kp orthonormal factor
     int* alive;    // batch x kp rank-guard flags
     double* gpart; // batch x row blocks x kp x kp Gram partials
     double* lfac;  // batch x kp x kp Cholesky factor, reciprocal pivots on its diagonal
     float* cmax;   // batch x row blocks x kp column maxima of the factors
+    bool shared;   // one of two halves of a call, run on two streams at once
 };
 
 // Largest rank the low-rank kernels accept.
 constexpr int kMaxRank = 64;
 
 // Fills the region pointers of one launch sequence over `batch` tensors for `base` (may
-// be null) and its size in *bytes.
-LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch,
+// be null) and its size in *bytes; `shared`: the sequence is one of a call's two halves.
+LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch, bool shared,
                                          size_t* bytes);
 // Workspace bytes of a whole call (a large call runs two halves, each with its own regions).
 size_t lowrank_workspace_total(int64_t m, int64_t n, int rank, int64_t batch);

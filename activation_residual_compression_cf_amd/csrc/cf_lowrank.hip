@@ -244,8 +244,8 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
 
 // ---------------------------------------------------------------- orth ----
 // orth(Y) in three launches:
-//   k_lr_gram   (batch x row blocks) Y = sum of the segment partials in segment
-//               order (fp32, written to `p` for the solve), and the fp64 Gram
+//   k_lr_gram   (batch x row blocks) Y = sum of the tensor's partials in order (fp32,
+//               written to `p` for the solve), and the fp64 Gram
 //               contribution Y_blk^T Y_blk of the block's rows (fp64 MFMA);
 //   k_lr_chol   (one workgroup per tensor) G = sum of the block Grams in block
 //               order; right-looking Cholesky G = L L^T in LDS with the rank guard
@@ -260,9 +260,13 @@ struct GramShape {
 };
 
 template <int KT>
+// The partials of Y: nwg == 0, those of a projection, nseg column segments per tensor
+// (Ypart[b][segment]); else those of a fused pass over nwg equal ranges of the batch's
+// list of `strips`-strip tensors (Ypart[2 w + 1] when tensor b is the second of workgroup
+// w's range, else Ypart[2 w]).
 __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart, float* __restrict__ p,
                                                   double* __restrict__ gpart, int64_t m, int64_t nseg,
-                                                  int64_t batch) {
+                                                  int64_t batch, int64_t nwg, int64_t strips) {
     constexpr int kp = GramShape<KT>::kp;
     constexpr int GR = GramShape<KT>::rows;
     __shared__ double ys[GR][kp + 1];
@@ -271,11 +275,30 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
     const int64_t blk = blockIdx.x % gblocks;
     const int64_t r0 = blk * GR;
     const int tid = threadIdx.x;
-    const float* yb = ypart + b * nseg * m * kp;
+    // partial 0 at y0, partial q >= 1 at y1 + (q - 1) ystep
+    const int64_t mk = m * kp;
+    const float *y0, *y1;
+    int64_t ystep;
+    if (nwg == 0) {
+        y0 = ypart + b * nseg * mk;
+        y1 = y0 + mk;
+        ystep = mk;
+    } else {
+        // the workgroups whose ranges hold the tensor's first and last strip: workgroup w
+        // starts at strip floor(w L / nwg), so strip x lies in floor(((x + 1) nwg - 1) / L)
+        const int64_t nlist = batch * strips, x0 = b * strips;
+        const int64_t wlo = ((x0 + 1) * nwg - 1) / nlist;
+        const int64_t whi = ((x0 + strips) * nwg - 1) / nlist;
+        const int64_t second = wlo * nlist / nwg < x0 ? 1 : 0;  // wlo's range began in tensor b - 1
+        nseg = whi - wlo + 1;
+        y0 = ypart + (2 * wlo + second) * mk;
+        y1 = ypart + 2 * (wlo + 1) * mk;
+        ystep = 2 * mk;
+    }
     float* pb = p + b * m * kp;
-    // Y = sum of the segment partials in segment order.  The loads of kSegBatch
-    // segments are issued together (indices past the last segment re-read it and are
-    // not added), so a thread waits for one batch at a time, not for every segment.
+    // Y = sum of the partials in order.  The loads of kSegBatch partials are issued
+    // together (indices past the last partial re-read it and are not added), so a thread
+    // waits for one batch at a time, not for every partial.
     constexpr int kEPT = GR * kp / 256;
     constexpr int kSegBatch = 3;
     float ysum[kEPT];
@@ -288,7 +311,7 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
             for (int j = 0; j < kEPT; ++j) {
                 const int e = tid + 256 * j;
                 const int64_t row = r0 + e / kp < m ? r0 + e / kp : m - 1;
-                v[qq][j] = yb[(q * m + row) * kp + e % kp];
+                v[qq][j] = (q == 0 ? y0 : y1 + (q - 1) * ystep)[row * kp + e % kp];
             }
         }
 #pragma unroll
@@ -613,64 +636,91 @@ __global__ __launch_bounds__(256) void k_lr_backproject(const float* r, const fl
 // projection) in one pass over r, which the two passes would otherwise read twice.  With r
 // strip-major a strip (16 columns of one tensor over all m rows) is one contiguous block,
 // and each 16 x 16 row tile of it is 1 KiB.
-// Workgroup: 8 waves over fused_strips(KT) consecutive strips of one tensor.  Wave w owns the
-// row tiles T = w + 8 jt (jt < RT) of every strip: it loads them (one 1 KiB run per
-// instruction) into registers a strip ahead, copies them into its own part of the LDS slot
-// once it is done with the strip before, and is the only wave that reads them, so the slot
-// needs no barrier.  Per strip:
+// The batch's strips, tensor after tensor, are one list (strip g of the list is at
+// r + g m 16, since each tensor's strips follow the last tensor's), cut into nwg equal ranges
+// of consecutive strips: workgroup w takes strips [w L / nwg, (w + 1) L / nwg) of the L in
+// the list.  nwg fills the chip in whole rounds of workgroups (fused_wgs), whatever the
+// batch, and nwg >= batch keeps a range within two tensors.
+// Workgroup: 8 waves.  Wave w owns the row tiles T = w + 8 jt (jt < RT) of every strip: it
+// loads them (one 1 KiB run per instruction) into registers a strip ahead, copies them into
+// its own part of the LDS slot once it is done with the strip before, and is the only wave
+// that reads them, so the slot needs no barrier.  Per strip:
 //   A  Q^T[kk][c] = sum over rows of P[row][kk] r[row][c]: MFMA 16x16x4 with P^T as the A
 //      operand (in registers for the whole workgroup) and 4 rows of a tile as B;
 //   the waves' partial Q^T tiles are summed in LDS in wave order (two barriers);
 //   B  Y[row][kk] += sum over the strip's columns of r[row][c] Q^T[kk][c]: a lane's float4
 //      of a row gives 4 k-slices, Q^T from LDS; the accumulators stay in registers over all
 //      of the workgroup's strips.
-// At the end each wave writes its rows of Y to Ypart[b][part] (part = the workgroup's strip
-// range), which the orthonormalisation sums in part order.  Used for m <= 1024 and padded
-// rank <= 32; RT = 2, 4 or 8 tiles per wave covers m <= 256, 512 or 1024.  Tiles past the
-// last row tile of the tensor re-read that tile: their P rows are zero, so they add exact
-// zeros to Q^T, and their Y rows are not stored.
+// Each wave writes its rows of the Y partial of the range's first tensor to Ypart[2 w] and,
+// if the range runs into the next tensor, of that tensor to Ypart[2 w + 1] (the P operands
+// are reloaded there); the orthonormalisation sums a tensor's partials in workgroup order.
+// Used for m <= 1024 and padded rank <= 32; RT = 2, 4 or 8 tiles per wave covers m <= 256,
+// 512 or 1024.  Tiles past the last row tile of the tensor re-read that tile: their P rows
+// are zero, so they add exact zeros to Q^T, and their Y rows are not stored.
 constexpr int kFusedWaves = 8;
-// Strips per workgroup: at rank <= 16 a workgroup takes 48 strips (fewer Y partials for the
-// orthonormalisation to read back, which pays at many iterations); at rank 17..32, whose
-// passes are longer, 24 strips leave a shorter last round of workgroups.
-constexpr int fused_strips(int64_t kt) { return kt == 1 ? 48 : 24; }
 constexpr int kFusedMaxRows = 1024;
+// Workgroups of the fused pass resident on one CU, from their registers (8 waves each;
+// RT = 8: 250-254 VGPRs, 2 waves per SIMD; RT = 4: 144-148, 3; RT = 2: 88-94, 5) and LDS
+// (26-86 KB), times the 256 CUs of an MI355X: one round of workgroups.  When the batch
+// runs as two halves on two streams (`shared`), a half's round is 7/8 of the chip: a pass
+// that takes every CU holds off the other stream's kernels until it ends, and the halves
+// then stop overlapping (FLUX shard, two halves: 224 workgroups a pass run r32/q2 at
+// 2.23-2.24 ms and r8/q10 at 4.13-4.18 ms; 232 or 256 run r8/q10 at 4.27-4.40 ms).
+constexpr int64_t kCUs = 256;
+constexpr int64_t fused_round(int64_t m, bool shared) { return kCUs * (m <= 256 ? 2 : 1) * (shared ? 7 : 8) / 8; }
+// Workgroups of one fused pass: whole rounds (the ranges are equal, so every workgroup of a
+// round ends at about the same time and no round runs part-empty), at least one per tensor,
+// and, where the batch is too small to fill a round, ranges of at least kp strips, so that a
+// range's Y partial (m kp floats, written once and read once) stays within 1/16 of the
+// r it reads (16 m floats per strip).
+constexpr int64_t fused_wgs(int64_t m, int64_t n, int64_t kp, int64_t batch, bool shared) {
+    const int64_t round = fused_round(m, shared);
+    const int64_t full = (batch + round - 1) / round * round;
+    const int64_t cap = (batch * (n >> 4) + kp - 1) / kp;
+    return full <= cap ? full : (cap > batch ? cap : batch);
+}
 
 template <int KT, int RT>
 __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* __restrict__ r,
                                                                    const float* __restrict__ p,
                                                                    float* __restrict__ ypart, int64_t m, int64_t n,
-                                                                   int64_t batch, int64_t nparts, int64_t total) {
+                                                                   int64_t batch, int64_t nwg, int64_t total) {
     constexpr int kp = 16 * KT;
     constexpr int kTile = 256;  // floats of one 16 x 16 tile
     __shared__ float slot[kFusedWaves * RT * kTile];  // wave w's tile jt at (w RT + jt) kTile
     __shared__ float red[kFusedWaves][KT][16][17];
     __shared__ float qs[kp][20];
     const int64_t lw = xcd_remap(blockIdx.x, total);
-    if (lw >= batch * nparts) return;  // uniform per workgroup
-    const int64_t b = lw / nparts, part = lw % nparts;
-    constexpr int kStrips = fused_strips(KT);
-    const int64_t s0 = part * kStrips;
-    const int64_t nstrips = n >> 4;
-    const int ns = static_cast<int>(nstrips - s0 < kStrips ? nstrips - s0 : kStrips);
+    if (lw >= nwg) return;  // uniform per workgroup
+    const int64_t S = n >> 4, nlist = batch * S;  // strips per tensor, in the list
+    const int64_t g0 = lw * nlist / nwg, g1 = (lw + 1) * nlist / nwg;
+    const int64_t b0 = g0 / S;  // the range's first tensor
+    const int ns = static_cast<int>(g1 - g0);
+    // strips of the first tensor (== ns when the range stays in it)
+    const int jb = static_cast<int>(((b0 + 1) * S < g1 ? (b0 + 1) * S : g1) - g0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
     const int mt = static_cast<int>(m >> 4);
-    const float* rs = r + b * m * n + s0 * (m << 4);  // the range's first strip
+    const float* rs = r + g0 * (m << 4);  // the range's first strip
 
     // this lane's 16 bytes of tile jt inside a strip
-    int toff[RT];
+    // (unsigned: a uniform base plus a zero-extended 32-bit offset is one load with a scalar
+    // base, so the addresses take no 64-bit vector registers)
+    unsigned toff[RT];
 #pragma unroll
     for (int jt = 0; jt < RT; ++jt) {
         const int T = wave + kFusedWaves * jt;
-        toff[jt] = (T < mt ? T : mt - 1) * kTile + 4 * lane;
+        toff[jt] = static_cast<unsigned>((T < mt ? T : mt - 1) * kTile + 4 * lane);
     }
-    // Strip j into the registers (nothing past the range: the copy of such a strip is never
-    // read), and the registers into this wave's part of the slot.  Strips loaded ahead: two
-    // at rank <= 16, one at rank 17..32 (whose registers are full).
+    // Strip j into the registers, and the registers into this wave's part of the slot.
+    // Strips loaded ahead: two at rank <= 16, one at rank 17..32 (whose registers are full).
+    // In the steady loops below every strip loads one (`sure`: the strip exists), so the
+    // compiler counts the loads in flight exactly and waits only for the strip it copies;
+    // a load skipped on some path would make it wait for every load at every strip.  Near
+    // the range's end nothing past the range is loaded (its copy would never be read).
     constexpr int kDepth = KT == 1 ? 2 : 1;
     vf4 stage[kDepth][RT];
-    auto fetch = [&](int j, vf4 (&st)[RT]) __attribute__((always_inline)) {
-        if (j >= ns) return;  // uniform per workgroup
+    auto fetch = [&](int j, vf4 (&st)[RT], bool sure) __attribute__((always_inline)) {
+        if (!sure && j >= ns) return;  // uniform per workgroup
         const float* src = rs + j * (m << 4);
 #pragma unroll
         for (int jt = 0; jt < RT; ++jt) st[jt] = ld_nt(src + toff[jt]);
@@ -681,25 +731,56 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
         for (int jt = 0; jt < RT; ++jt) *reinterpret_cast<vf4*>(ws + jt * kTile + 4 * lane) = st[jt];
     };
 
-    // P^T operands of A.  Lane: P[16 T + 4 c + lg][16 t + li] for tile jt, chunk c.
-    const float* pb = p + b * m * kp;
+    // P^T operands of A for tensor b, and Y's accumulators set to zero.  Lane:
+    // P[16 T + 4 c + lg][16 t + li] for tile jt, chunk c.
     float pv[RT][4][KT];
     vf4 acc[RT][KT];
+    auto begin_tensor = [&](int64_t b) __attribute__((always_inline)) {
+        const float* pb = p + b * m * kp;
 #pragma unroll
-    for (int jt = 0; jt < RT; ++jt) {
-        const int T = wave + kFusedWaves * jt;
+        for (int jt = 0; jt < RT; ++jt) {
+            const int T = wave + kFusedWaves * jt;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) acc[jt][t] = vf4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < KT; ++t) acc[jt][t] = vf4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int t = 0; t < KT; ++t) pv[jt][c][t] = T < mt ? pb[(16 * T + 4 * c + lg) * kp + 16 * t + li] : 0.0f;
-    }
-    fetch(0, stage[0]);
+                for (int t = 0; t < KT; ++t)
+                    pv[jt][c][t] = T < mt ? pb[(16 * T + 4 * c + lg) * kp + 16 * t + li] : 0.0f;
+        }
+    };
+    // acc[jt][t] lane: Y rows 16 T + 4 lg + v, column 16 t + li
+    auto store_y = [&](int seg) __attribute__((always_inline)) {
+        float* yp = ypart + (2 * lw + seg) * m * kp;
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) {
+            const int T = wave + kFusedWaves * jt;
+            if (T < mt)
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) yp[(16 * T + 4 * lg + v) * kp + 16 * t + li] = acc[jt][t][v];
+        }
+    };
+    begin_tensor(b0);
+    fetch(0, stage[0], true);
     put(stage[0]);
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) fetch(1 + d, stage[d]);
-    auto strip = [&](int j, vf4 (&st)[RT]) __attribute__((always_inline)) {
+    for (int d = 0; d < kDepth; ++d) fetch(1 + d < ns ? 1 + d : ns - 1, stage[d], true);  // the copy past ns is unread
+    // The change to the next tensor: Y of the first goes out, the new P operands come in,
+    // and the wave waits for them right here (a load still in flight where two paths meet
+    // would make the compiler wait for every load at every strip).
+    auto next_tensor = [&]() __attribute__((always_inline)) {
+        store_y(0);
+        begin_tensor(b0 + 1);
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int t = 0; t < KT; ++t) asm volatile("" ::"v"(pv[jt][c][t]));
+    };
+    auto strip = [&](int j, vf4 (&st)[RT], bool sure) __attribute__((always_inline)) {
         // A: this wave's partial Q^T of the strip (two accumulator sets per tile column)
         vf4 qa[2][KT];
 #pragma unroll
@@ -744,29 +825,48 @@ __global__ __launch_bounds__(64 * kFusedWaves) void k_lr_backfore(const float* _
         // strip j + 2 start.  (The next writes of red and qs follow the next strip's barriers,
         // which every wave reaches only after its reads of them above.)
         put(st);
-        fetch(j + 1 + kDepth, st);
+        fetch(j + 1 + kDepth, st, sure);
     };
+    // The range's strips, one tensor at a time.  The change of tensor sits outside the strip
+    // loops: a branch inside them, even one never taken, costs the loops register copies and
+    // scalar work at every strip.
     if constexpr (kDepth == 2) {
-        int j = 0;
-        for (; j + 1 < ns; j += 2) {
-            strip(j, stage[0]);
-            strip(j + 1, stage[1]);
+        // strips [j, j1) of a tensor start with strip j + 1 in stage[0] and j + 2 in stage[1]
+        int j = 0, j1 = jb;
+        for (;;) {
+            for (; j + 1 < j1 && j + 4 < ns; j += 2) {
+                strip(j, stage[0], true);
+                strip(j + 1, stage[1], true);
+            }
+            for (; j + 1 < j1; j += 2) {
+                strip(j, stage[0], false);
+                strip(j + 1, stage[1], false);
+            }
+            const bool odd = j < j1;  // uniform per workgroup
+            if (odd) strip(j++, stage[0], false);
+            if (j1 == ns) break;
+            next_tensor();
+            if (odd) {  // one strip past the pairs: the next strip's copy is in stage[1]
+#pragma unroll
+                for (int jt = 0; jt < RT; ++jt) {
+                    const vf4 x = stage[0][jt];
+                    stage[0][jt] = stage[1][jt];
+                    stage[1][jt] = x;
+                }
+            }
+            j1 = ns;
         }
-        if (j < ns) strip(j, stage[0]);
-    } else {
-        for (int j = 0; j < ns; ++j) strip(j, stage[0]);
+    } else {  // (as one loop over the tensors, the rank 17..32 body spills)
+        int j = 0;
+        for (; j < jb && j + 2 < ns; ++j) strip(j, stage[0], true);
+        for (; j < jb; ++j) strip(j, stage[0], false);
+        if (jb < ns) {
+            next_tensor();
+            for (; j + 2 < ns; ++j) strip(j, stage[0], true);
+            for (; j < ns; ++j) strip(j, stage[0], false);
+        }
     }
-    // acc[jt][t] lane: Y rows 16 T + 4 lg + v, column 16 t + li
-    float* yp = ypart + (b * nparts + part) * m * kp;
-#pragma unroll
-    for (int jt = 0; jt < RT; ++jt) {
-        const int T = wave + kFusedWaves * jt;
-        if (T < mt)
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) yp[(16 * T + 4 * lg + v) * kp + 16 * t + li] = acc[jt][t][v];
-    }
+    store_y(jb < ns ? 1 : 0);
 }
 
 // ------------------------------------------------------------ quantize ----
@@ -1196,12 +1296,12 @@ int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 // share this computation.  Every workgroup has 256 threads (kCholThreads for the
 // factorisation, one workgroup per tensor).
 struct LowrankGrids {
-    int64_t kp, nseg, nparts, gblocks;
+    int64_t kp, nseg, fwgs, gblocks;  // fwgs: workgroups (strip ranges) of a fused pass
     int64_t project_first, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
     bool fused;  // iterations after the first run the fused pass
 };
 
-LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
+LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch, bool shared = false) {
     LowrankGrids g;
     g.kp = (rank + 15) / 16 * 16;
     g.nseg = (n + kSegCols - 1) / kSegCols;
@@ -1213,8 +1313,8 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch) {
     g.solve = batch * ((m + 255) / 256);
     g.backproject = round8(batch * ((n + kBackCols - 1) / kBackCols));
     g.fused = g.kp <= 32 && m <= kFusedMaxRows;
-    g.nparts = (n / 16 + fused_strips(g.kp / 16) - 1) / fused_strips(g.kp / 16);
-    g.backfore = round8(batch * g.nparts);
+    g.fwgs = fused_wgs(m, n, g.kp, batch, shared);
+    g.backfore = round8(g.fwgs);
     g.quant = batch * ((m + 255) / 256 + (n + 255) / 256);
     g.reconstruct = round8(batch * ((m + kRecRows - 1) / kRecRows) * ((n + kRecCols - 1) / kRecCols));
     return g;
@@ -1250,7 +1350,7 @@ template <typename ActT, int KT>
 hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_t n, int k, int iters,
                        int factor_bits, int64_t batch, float* q_state, void* u, float* u_scales, void* v,
                        float* v_scales, const LowrankWorkspace& ws, hipStream_t stream, hipEvent_t after_first) {
-    const LowrankGrids grid = lowrank_grids(m, n, k, batch);
+    const LowrankGrids grid = lowrank_grids(m, n, k, batch, ws.shared);
     int64_t nseg = grid.nseg;
     hipError_t e;
     int64_t ptotal = grid.project;
@@ -1258,7 +1358,9 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     int64_t ftotal = grid.backfore;
     int64_t mblk = (m + 255) / 256;               // U blocks of the quantizer per tensor
     int64_t nblk = mblk + (n + 255) / 256;        // U and V blocks
-    int64_t nparts = grid.nparts;
+    int64_t fwgs = grid.fwgs;
+    int64_t strips = n >> 4;
+    int64_t none = 0;
     const bool fused = KT <= 2 && grid.fused;
     int64_t pftotal = grid.project_first;
     void* pfargs[] = {&a, &ahat, (void*)&ws.r, (void*)&q_state, (void*)&ws.ypart, &m, &n, &batch, &nseg, &pftotal, &k};
@@ -1268,9 +1370,9 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
     for (int it = 0; it < iters; ++it) {
         // orth of Y: its partials come from the column segments of a projection, or from
         // the strip ranges of a fused pass
-        int64_t parts = it > 0 && fused ? nparts : nseg;
         int64_t gblocks = grid.gblocks;
-        void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &parts, &batch};
+        void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch,
+                         it > 0 && fused ? (void*)&fwgs : (void*)&none, &strips};
         if ((e = go(&k_lr_gram<KT>, grid.gram, gargs, stream)) != hipSuccess) return e;
         void* cargs[] = {(void*)&ws.gpart, (void*)&ws.lfac, (void*)&ws.alive, &gblocks, &k};
         if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>),
@@ -1287,7 +1389,7 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
             if ((e = go(&k_lr_backproject<KT>, btotal, bargs, stream)) != hipSuccess) return e;
         } else if (fused) {     // Q of this iteration and Y of the next in one pass
             if constexpr (KT <= 2) {
-                void* fargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.ypart, &m, &n, &batch, &nparts, &ftotal};
+                void* fargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.ypart, &m, &n, &batch, &fwgs, &ftotal};
                 const void* fk = m <= 256   ? reinterpret_cast<const void*>(&k_lr_backfore<KT, 2>)
                                  : m <= 512 ? reinterpret_cast<const void*>(&k_lr_backfore<KT, 4>)
                                             : reinterpret_cast<const void*>(&k_lr_backfore<KT, 8>);
@@ -1335,16 +1437,18 @@ hipError_t dispatch_rank(const ActT* a, float* ahat, float* err, int64_t m, int6
 // second on a side stream that starts once the first half's first projection is done.
 // The halves then stand about one streaming pass apart, so the latency-bound kernels of
 // one (orthonormalisation, factor quantization) run while the other streams r, and the
-// ramp and drain of each pass overlaps the other half's work.  Each tensor's arithmetic
-// is the same as in one launch sequence, so the results are identical.  The side
-// stream has the default priority; the caller's stream waits for it before the call's
-// later work.  Calls below this size run as one sequence: the event round trips would
-// cost more than the overlap gains.
+// ramp and drain of each pass overlaps the other half's work.  The side stream has the
+// default priority; the caller's stream waits for it before the call's later work.
+// Calls below this size run as one sequence: the event round trips would cost more than
+// the overlap gains.  So do calls at rank <= 16, whose orthonormalisation is short and
+// whose fused passes run best over the whole batch (FLUX shard, one sequence against two
+// halves: r8/q10 4.04-4.07 against 4.08-4.10 ms, r16/q4 2.54 against 2.58; at rank 32 the
+// halves win, r32/q2 2.23-2.24 against 2.29, r32/q10 5.47-5.52 against 5.75).
 constexpr int64_t kSplitElems = int64_t(1) << 24;
 
 // Tensors in the first half, or 0 for one sequence.
-int64_t split_first_half(int64_t m, int64_t n, int64_t batch) {
-    return batch >= 2 && m * n * batch >= kSplitElems ? (batch + 1) / 2 : 0;
+int64_t split_first_half(int64_t m, int64_t n, int rank, int64_t batch) {
+    return batch >= 2 && rank > 16 && m * n * batch >= kSplitElems ? (batch + 1) / 2 : 0;
 }
 
 // The side stream and the two events of one host thread on one device, made on first use
@@ -1383,9 +1487,9 @@ hipError_t run_split(const ActT* a, float* ahat, float* err, int64_t m, int64_t 
     hipError_t e = split_sync(&sync);
     if (e != hipSuccess) return e;
     size_t bytes_first = 0;
-    const LowrankWorkspace ws1 = carve_lowrank_workspace(workspace, m, n, k, half, &bytes_first);
+    const LowrankWorkspace ws1 = carve_lowrank_workspace(workspace, m, n, k, half, true, &bytes_first);
     const LowrankWorkspace ws2 =
-        carve_lowrank_workspace(static_cast<char*>(workspace) + bytes_first, m, n, k, batch - half, nullptr);
+        carve_lowrank_workspace(static_cast<char*>(workspace) + bytes_first, m, n, k, batch - half, true, nullptr);
     const int64_t mn = m * n, fb8 = factor_bits;  // factor bits per (row, rank) pair
     if ((e = dispatch_rank(a, ahat, err, m, n, k, iters, factor_bits, half, q_state, u, u_scales, v, v_scales, ws1,
                            stream, sync->first_done)) != hipSuccess)
@@ -1405,25 +1509,26 @@ hipError_t run_split(const ActT* a, float* ahat, float* err, int64_t m, int64_t 
 
 size_t lowrank_workspace_total(int64_t m, int64_t n, int rank, int64_t batch) {
     size_t one = 0, two = 0;
-    const int64_t half = split_first_half(m, n, batch);
+    const int64_t half = split_first_half(m, n, rank, batch);
     if (!half) {
-        carve_lowrank_workspace(nullptr, m, n, rank, batch, &one);
+        carve_lowrank_workspace(nullptr, m, n, rank, batch, false, &one);
         return one;
     }
-    carve_lowrank_workspace(nullptr, m, n, rank, half, &one);
-    carve_lowrank_workspace(nullptr, m, n, rank, batch - half, &two);
+    carve_lowrank_workspace(nullptr, m, n, rank, half, true, &one);
+    carve_lowrank_workspace(nullptr, m, n, rank, batch - half, true, &two);
     return one + two;
 }
 
-LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch, size_t* bytes) {
+LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int rank, int64_t batch, bool shared,
+                                         size_t* bytes) {
     const int64_t kp = (rank + 15) / 16 * 16;
     const int64_t nseg = (n + kSegCols - 1) / kSegCols;
-    const int64_t gblocks = lowrank_grids(m, n, rank, batch).gblocks;
+    const int64_t gblocks = lowrank_grids(m, n, rank, batch, shared).gblocks;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     const int64_t sz_r = up(batch * m * n * 4);
     const int64_t sz_qt = up(batch * kp * n * 4);
-    const LowrankGrids g = lowrank_grids(m, n, rank, batch);
-    const int64_t sz_y = up(batch * (g.fused && g.nparts > nseg ? g.nparts : nseg) * m * kp * 4);
+    const LowrankGrids g = lowrank_grids(m, n, rank, batch, shared);
+    const int64_t sz_y = up((g.fused && 2 * g.fwgs > batch * nseg ? 2 * g.fwgs : batch * nseg) * m * kp * 4);
     const int64_t sz_p = up(batch * m * kp * 4);
     const int64_t sz_al = up(batch * kp * 4);
     const int64_t sz_g = up(batch * gblocks * kp * kp * 8);
@@ -1431,6 +1536,7 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
     const int64_t sz_c = up(batch * ((m + 255) / 256 + (n + 255) / 256) * kp * 4);
     if (bytes) *bytes = static_cast<size_t>(sz_r + sz_qt + sz_y + sz_p + sz_al + sz_g + sz_x + sz_c);
     LowrankWorkspace ws{};
+    ws.shared = shared;
     if (base) {
         char* c = static_cast<char*>(base);
         ws.r = reinterpret_cast<float*>(c);
@@ -1465,14 +1571,14 @@ hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, floa
                                    int rank, int iters, int factor_bits, int64_t batch, float* q_state, void* u,
                                    float* u_scales, void* v, float* v_scales, void* workspace,
                                    hipStream_t stream) {
-    if (const int64_t half = split_first_half(m, n, batch)) {
+    if (const int64_t half = split_first_half(m, n, rank, batch)) {
         if (a_dtype == 0)
             return run_split(static_cast<const uint16_t*>(a), ahat, err, m, n, rank, iters, factor_bits, batch,
                              q_state, u, u_scales, v, v_scales, workspace, half, stream);
         return run_split(static_cast<const float*>(a), ahat, err, m, n, rank, iters, factor_bits, batch, q_state, u,
                          u_scales, v, v_scales, workspace, half, stream);
     }
-    const LowrankWorkspace ws = carve_lowrank_workspace(workspace, m, n, rank, batch, nullptr);
+    const LowrankWorkspace ws = carve_lowrank_workspace(workspace, m, n, rank, batch, false, nullptr);
     if (a_dtype == 0)
         return dispatch_rank(static_cast<const uint16_t*>(a), ahat, err, m, n, rank, iters, factor_bits, batch,
                              q_state, u, u_scales, v, v_scales, ws, stream, nullptr);

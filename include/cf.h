@@ -204,7 +204,9 @@ int cf_topk_decompress(int k, const uint8_t* idx, const uint16_t* vals, float* a
  *   every kernel grid within a dispatch's 2^32 - 1 work-items (only extreme shapes,
  *   such as a single row block of 2^28 columns, reach that); CF_E_SHAPE otherwise.
  *   a, ahat, err 16-byte aligned; the other pointers 4-byte aligned.
- * Arithmetic is fp32 (fp64 inside orth); results are deterministic.
+ * Arithmetic is fp32 (fp64 inside orth).  Results are deterministic for given shapes,
+ * rank, iters and batch; a tensor's last bits depend on the batch it is sent in, since
+ * the fp32 sums of Y follow the work's split of the whole batch into equal parts.
  */
 int cf_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,
                         int rank, int iters, int factor_bits, int batch, float* q_state, void* u,

@@ -368,31 +368,44 @@ def test_flux_whole_trajectory(cf, dev, O, rank, iters, samples):
 
 
 @pytest.mark.parametrize("batch", [7, 16])
-def test_split_call_matches_one_call_per_tensor(cf, dev, batch):
-    """A call of 7 or 16 FLUX-shard tensors (22M or 50M elements) runs as two halves on two
-    streams; one call per tensor runs as a single launch sequence.  Every output of every
-    tensor (reconstruction, error, q_state, payload) is the same bit for bit."""
-    m, n, k = 1024, 3072, 32
+def test_split_call(cf, dev, O, batch):
+    """A call of 7 or 16 FLUX-shard tensors (22M or 50M elements) at rank 32 runs as two
+    halves on two streams.  The tensors on both sides of the cut and at the ends agree
+    with the oracle from the same state (fp32 factors, 2e-4), err == a - Ahat and the
+    receiver equals the sender on every element, and the same call from the same state
+    gives the same bits again."""
+    m, n, k, iters = 1024, 3072, 32, 2
     wl = gen.Workload("split", m, n, batch, 2, "bf16", True)
     tr = gen.Trajectory(wl, 17)
-    A0, A1 = (to_dev(tr.next(), dev).view(batch, m, n) for _ in range(2))
+    A0_host, A1_host = tr.next(), tr.next()
+    A0, A1 = (to_dev(x, dev).view(batch, m, n) for x in (A0_host, A1_host))
     q0 = torch.from_numpy(start_bases(17, batch, n, k)).to(dev)
-    say(f"two-stream call of {batch} tensors against one call per tensor")
-    ah = torch.empty((batch, m, n), dtype=torch.float32, device=dev)
-    er = torch.empty_like(ah)
-    cf.init_state(A0, ah, er)
-    q = q0.clone()
-    pay = cf.lowrank_compress(A1, ah, er, q, k, 2, 4)
-    ah1 = torch.empty_like(ah)
-    er1 = torch.empty_like(ah)
-    cf.init_state(A0, ah1, er1)
-    q1 = q0.clone()
-    pays = [cf.lowrank_compress(A1[b:b + 1], ah1[b:b + 1], er1[b:b + 1], q1[b:b + 1], k, 2, 4) for b in range(batch)]
+    say(f"two-stream call of {batch} tensors")
+    ah0 = torch.empty((batch, m, n), dtype=torch.float32, device=dev)
+    cf.init_state(A0, ah0, torch.empty_like(ah0))
+    outs = []
+    for _ in range(2):
+        ah, er, q = ah0.clone(), torch.empty_like(ah0), q0.clone()
+        pay = cf.lowrank_compress(A1, ah, er, q, k, iters, 32)
+        torch.cuda.synchronize()
+        outs.append((ah, er, q, pay))
+    ah, er, q, pay = outs[0]
+    for x, y in zip((ah, er, q, *pay), (outs[1][0], outs[1][1], outs[1][2], *outs[1][3])):
+        assert (x is None and y is None) or torch.equal(x, y), "a repeated call differs"  # no scales at fp32
+    assert torch.equal(er, A1.float() - ah), "err != a - ahat"
+    rx = ah0.clone()
+    cf.lowrank_decompress(32, pay, rx, k)
     torch.cuda.synchronize()
-    for x, y in ((ah, ah1), (er, er1), (q, q1)):
-        assert torch.equal(x, y)
-    for i in range(4):
-        assert torch.equal(pay[i], torch.cat([p[i] for p in pays]))
+    assert torch.equal(rx, ah), "receiver differs from sender"
+    half = (batch + 1) // 2
+    for s in sorted({0, half - 1, half, batch - 1}):
+        ah_o, q_o = host(ah0[s]).copy(), host(q0[s]).copy()
+        O.lowrank_compress(np.ascontiguousarray(A1_host[s]), ah_o, np.zeros_like(ah_o), q_o, k, iters, 32)
+        before = host(ah0[s]).astype(np.float64)
+        e = rel(host(ah[s]).astype(np.float64) - before, ah_o.astype(np.float64) - before)
+        eq = rel(host(q[s]), q_o)
+        say(f"  tensor {s}: rel(R_gpu, R_oracle) = {e:.2e}, rel(q_state) = {eq:.2e}")
+        assert e <= 2e-4 and eq <= 2e-4, f"tensor {s}"
 
 
 def test_deterministic(cf, dev):
