@@ -162,6 +162,29 @@ def test_step_parity_fused_pass_shapes(cf, dev, O, m, n, rank, iters, fb):
         prev = A
 
 
+@pytest.mark.parametrize("m,n,rank,iters,fb", [(256, 640, 8, 3, 4), (512, 1040, 16, 2, 32), (256, 640, 32, 2, 16)])
+def test_step_parity_fused_ranges_across_tensors(cf, dev, O, m, n, rank, iters, fb):
+    """The fused pass cuts the batch's strips into equal ranges that run into the next
+    tensor.  Three tensors of 40 or 65 strips: 8 ranges of 15 strips at rank 8 (two of them
+    change tensor after 10 and 5 strips, an even and an odd count at two strips loaded
+    ahead), 13 ranges at rank 16 (changes after 5 and 10 strips), 4 ranges of 30 strips at
+    rank 32 (one strip ahead); every tensor against the oracle, 2 steps."""
+    wl = gen.Workload("lrr", m, n, 3, 3, "bf16", True)
+    say(f"lowrank fused ranges across tensors: {m}x{n} rank={rank} iters={iters} fb={fb}")
+    tr = gen.Trajectory(wl, 5)
+    A0 = tr.next()
+    ahat = torch.empty((3, m, n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(to_dev(A0, dev), ahat, err)
+    qs = torch.from_numpy(start_bases(5, 3, n, rank)).to(dev)
+    prev = A0
+    for t in range(1, 3):
+        A = tr.next()
+        check_step(cf, dev, O, prev, A, ahat, err, qs, rank, iters, fb, samples=[0, 1, 2],
+                   tol=2e-4 if fb == 32 else 1e-3, cold=t == 1)
+        prev = A
+
+
 def test_int4_stage_isolated(cf, dev, O):
     """The INT4 codes and scales equal the oracle's quantizer on the GPU's fp32 factors."""
     wl = gen.Workload("lr", 256, 768, 2, 2, "bf16", True)
