@@ -130,6 +130,7 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
     const int64_t rb = (lw / nseg) % rblocks;
     const int64_t sgi = lw % nseg;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int li = lane & 15, lg = lane >> 4;
     const int64_t c0 = sgi * kSegCols;
     const int64_t mn = m * n;
@@ -208,9 +209,10 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
 #pragma unroll
             for (int i = 0; i < kSegCols / 64; ++i) {
                 const int st = 4 * i + wave;
+                const int sst = 4 * i + wave_s;  // the same strip, in scalar registers
                 if (c0 + 16 * st < n)
-                    st_nt(r + b * mn + strip_off(m, sr + (lane >> 2), c0 + 16 * st + 4 * (lane & 3)),
-                          *reinterpret_cast<const vf4*>(&slab[lane >> 2][16 * st + 4 * (lane & 3)]));
+                    st_stream_run(r + b * mn + strip_off(m, sr, c0 + 16 * sst),
+                                  *reinterpret_cast<const vf4*>(&slab[lane >> 2][16 * st + 4 * (lane & 3)]));
             }
         }
         if (sr + kStage < rend) fetch(sr + kStage);  // next stage's loads overlap the MFMAs
@@ -1094,6 +1096,7 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     const int64_t r0 = ((lw / cblocks) % rblocks) * kRecRows;
     const int64_t c0 = (lw % cblocks) * kRecCols;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int li = lane & 15, lg = lane >> 4;
 
     const int64_t usz = m * k * FB / 8;  // bytes per tensor
@@ -1244,10 +1247,11 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int rr = 4 * wave + q;
-                const int64_t off = b * mn + (r0 + kStage * st + rr) * n + col;
+                // the row's run of 256 columns, its address in scalar registers
+                const int64_t run = b * mn + (r0 + kStage * st + 4 * wave_s + q) * n + c0;
                 const vf4 hn = hb[st & 1][q] + *reinterpret_cast<const vf4*>(&tile[rr][4 * lane]);
-                st_nt(ahat + off, hn);
-                if constexpr (HAS_E) st_nt(err + off, RA::cvt(xb[st & 1][q]) - hn);
+                st_stream_run(ahat + run, hn);
+                if constexpr (HAS_E) st_stream_run(err + run, RA::cvt(xb[st & 1][q]) - hn);
             }
             if (st + 2 < kNS) fill(hb[st & 1], xb[st & 1], st + 2);
             __syncthreads();

@@ -231,6 +231,10 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
     const int64_t g0 = tile * (2 * IPS) + (lane >> 5);
     if (tile * (2 * IPS) >= ngroups) return;  // uniform per wave
 
+    // the tile's first element, and stream resources over its 256*IPS elements of state
+    const int64_t t0 = wave_uniform(tile) * (2 * IPS) * kGroup;
+    const __amdgpu_buffer_rsrc_t rs_h = stream_rsrc(ahat + t0, 2 * IPS * kGroup * 4);
+    const __amdgpu_buffer_rsrc_t rs_e = stream_rsrc(err ? err + t0 : nullptr, 2 * IPS * kGroup * 4);
     vf4 x[IPS], h[IPS];
     int64_t gi[IPS];
     bool ok[IPS];
@@ -296,10 +300,10 @@ __global__ __launch_bounds__(BLOCK) void k_compress(const ActT* __restrict__ a, 
         }
 
         if (ok[k]) {
-            const int64_t off = gi[k] * kGroup + hl * 4;
-            st_nt(ahat + off, hn);
+            const uint32_t boff = static_cast<uint32_t>(gi[k] * kGroup + hl * 4 - t0) * 4u;  // within the tile
+            st_stream(rs_h, boff, hn);
             if constexpr (MODE == kEF) {
-                if (err) st_nt(err + off, e);  // the error buffer is optional (wave-uniform test)
+                if (err) st_stream(rs_e, boff, e);  // the error buffer is optional (wave-uniform test)
             }
             if constexpr (BITS == 1) {
                 if ((hl & 7) == 0) *reinterpret_cast<uint32_t*>(codes + gi[k] * 16 + (hl >> 1)) = w;
@@ -347,9 +351,9 @@ __global__ __launch_bounds__(BLOCK) void k_decompress(const uint8_t* __restrict_
     for (int k = 0; k < IPS; ++k) {
         const vf4 hn = h[k] + dequant4<BITS>(code[k], s[k]);
         if (ok[k]) {
-            const int64_t off = gi[k] * kGroup + hl * 4;
-            st_nt(ahat + off, hn);
-            if constexpr (OUT16) __builtin_nontemporal_store(to_bf16x4(hn), reinterpret_cast<vu2*>(out + off));
+            const int64_t run = wave_uniform((g0 - (lane >> 5) + 2 * k) * kGroup);  // the two groups' first element
+            st_stream_run(ahat + run, hn);
+            if constexpr (OUT16) st_stream_run8(out + run, to_bf16x4(hn));
         }
     }
 }
@@ -360,8 +364,16 @@ __global__ __launch_bounds__(BLOCK) void k_init(const ActT* __restrict__ a, floa
                                                  float* __restrict__ err, int64_t nquads) {
     const int64_t q = static_cast<int64_t>(blockIdx.x) * BLOCK + threadIdx.x;
     if (q >= nquads) return;
-    st_nt(ahat + q * 4, load_act4(a, q * 4));
-    if (err) st_nt(err + q * 4, vf4{0.f, 0.f, 0.f, 0.f});
+    // the wave's first element (its quads are consecutive), in scalar registers
+    const int64_t w0 = wave_uniform((q - (threadIdx.x & 63)) * 4);
+    const vf4 x = load_act4(a, q * 4);
+    if ((static_cast<int64_t>(blockIdx.x) * BLOCK + (threadIdx.x & ~63u) + 64) <= nquads) {
+        st_stream_run(ahat + w0, x);
+        if (err) st_stream_run(err + w0, vf4{0.f, 0.f, 0.f, 0.f});
+    } else {  // the wave at the end of a ragged tail
+        st_nt(ahat + q * 4, x);
+        if (err) st_nt(err + q * 4, vf4{0.f, 0.f, 0.f, 0.f});
+    }
 }
 
 // Decode calls of at least this many groups (about 8 FLUX-shard tensors) take the large

@@ -141,9 +141,9 @@ __device__ __forceinline__ void topk_group(RawT raw, vf2 h, int64_t g, int lane,
     const uint32_t v0 = bf16_rne(r0), v1 = bf16_rne(r1);
     const float hn0 = sel0 ? h.x + bf16_widen(v0) : h.x;
     const float hn1 = sel1 ? h.y + bf16_widen(v1) : h.y;
-    const int64_t off = g * kGroup + lane * 2;
-    __builtin_nontemporal_store(vf2{hn0, hn1}, reinterpret_cast<vf2*>(ahat + off));
-    if constexpr (HAS_E) __builtin_nontemporal_store(vf2{x.x - hn0, x.y - hn1}, reinterpret_cast<vf2*>(err + off));
+    // the group's 512-byte runs of state (g is the same in every lane)
+    st_stream_run8(ahat + g * kGroup, vf2{hn0, hn1});
+    if constexpr (HAS_E) st_stream_run8(err + g * kGroup, vf2{x.x - hn0, x.y - hn1});
     pay.put(slot0, sel0, lane * 2, v0);
     pay.put(slot1, sel1, lane * 2 + 1, v1);
 }
@@ -267,8 +267,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_decompress(const uint8_t* __rest
         const uint32_t w0 = table[wave][lane * 2], w1 = table[wave][lane * 2 + 1];
         const float hn0 = (w0 & 0xffff0000u) == tag ? h[j].x + bf16_widen(w0 & 0xffffu) : h[j].x;
         const float hn1 = (w1 & 0xffff0000u) == tag ? h[j].y + bf16_widen(w1 & 0xffffu) : h[j].y;
-        if (g0 + j < ngroups)
-            __builtin_nontemporal_store(vf2{hn0, hn1}, reinterpret_cast<vf2*>(ahat + (g0 + j) * kGroup + lane * 2));
+        if (g0 + j < ngroups) st_stream_run8(ahat + (g0 + j) * kGroup, vf2{hn0, hn1});
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

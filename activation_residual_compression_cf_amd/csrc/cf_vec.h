@@ -11,6 +11,8 @@ namespace cf {
 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef unsigned vu2 __attribute__((ext_vector_type(2)));
+typedef int vi4 __attribute__((ext_vector_type(4)));
+typedef int vi2 __attribute__((ext_vector_type(2)));
 
 // Non-temporal accesses: every byte of the streamed state is touched once per
 // step, so nothing is worth keeping in L2.
@@ -19,6 +21,44 @@ __device__ __forceinline__ vf4 ld_nt(const float* p) {
 }
 __device__ __forceinline__ void st_nt(float* p, vf4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<vf4*>(p));
+}
+
+// Streaming stores through a buffer resource, at device scope and non-temporal (cache
+// policy sc1 nt).  A wave builds the resource from a base address it holds in scalar
+// registers (one that is the same in every lane: a kernel argument plus a block or
+// wave index) and a byte length; each lane passes its byte offset from that base.
+// Stores at or past the length are dropped by the hardware.  Measured on a FLUX step
+// of the 14-byte-per-element sender pattern, these stores run about 1.5% faster than
+// plain non-temporal stores.
+constexpr int kStorePolicy = 1 << 1 /* nt */ | 1 << 4 /* sc1 */;
+// A value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t wave_uniform(int64_t v) {
+    const uint64_t u = static_cast<uint64_t>(v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(void* base, uint32_t bytes) {
+    // dword 3 of a gfx9 buffer resource: 32-bit data format, the one raw accesses need
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void st_stream(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, vf4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vi4, v), r, byte_off, 0, kStorePolicy);
+}
+
+// One wave instruction's streaming store of a 1 KiB run: lane l writes bytes
+// 16 l .. 16 l + 15 of the run that starts at `run`, an address that must be the same
+// in every lane.
+__device__ __forceinline__ void st_stream_run(float* run, vf4 v) {
+    st_stream(stream_rsrc(run, 1024), (threadIdx.x & 63u) * 16u, v);
+}
+
+// The same for 8 bytes per lane: a 512-byte run.
+template <typename V8>
+__device__ __forceinline__ void st_stream_run8(void* run, V8 v) {
+    static_assert(sizeof(V8) == 8, "8 bytes per lane");
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(vi2, v), stream_rsrc(run, 512),
+                                          (threadIdx.x & 63u) * 8u, 0, kStorePolicy);
 }
 
 // 4 consecutive activations at element offset `off`, widened to fp32 (exact).
