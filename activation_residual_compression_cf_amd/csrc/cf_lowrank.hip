@@ -26,8 +26,8 @@
 //                   and stores r, and reads Q from q_state (rank padded to a multiple of
 //                   16 with zeros).  fp32 MFMA 16x16x4: a lane's float4 of r supplies
 //                   4 k-slices, Q^T float4s the matching B operands.
-//   k_lr_gram, k_lr_chol, k_lr_solve  orth: Y = sum of partials (fixed order), fp64
-//                   Gram, Cholesky with the rank guard, P = Y R^-1; the last solve also
+//   k_lr_gram, k_lr_solve  orth: Y = sum of partials (fixed order), fp64 Gram; then
+//                   Cholesky with the rank guard and P = Y R^-1; the last solve also
 //                   writes U's column maxima for the quantizer.
 //   k_lr_backproject Q^T = P^T r, MFMA; each wave of a workgroup owns 64 of its 256
 //                   columns over every row; the last one also writes V's column maxima.
@@ -245,15 +245,15 @@ __global__ __launch_bounds__(256) void k_lr_project(const ActT* __restrict__ a, 
 }
 
 // ---------------------------------------------------------------- orth ----
-// orth(Y) in three launches:
+// orth(Y) in two launches:
 //   k_lr_gram   (batch x row blocks) Y = sum of the tensor's partials in order (fp32,
 //               written to `p` for the solve), and the fp64 Gram
 //               contribution Y_blk^T Y_blk of the block's rows (fp64 MFMA);
-//   k_lr_chol   (one workgroup per tensor) G = sum of the block Grams in block
+//   k_lr_solve  (batch x blocks of 256 rows) G = sum of the block Grams in block
 //               order; right-looking Cholesky G = L L^T in LDS with the rank guard
-//               (pivot <= 1e-10 trace(G) -> dead column);
-//   k_lr_solve  (batch x row blocks) P[row] = Y[row] L^-T by forward substitution
-//               in fp64, in place over Y.
+//               (pivot <= 1e-10 trace(G) -> dead column), the same in every workgroup
+//               of a tensor; then P[row] = Y[row] L^-T by forward substitution in
+//               fp64, in place over Y.
 constexpr int64_t gram_rows(int64_t kt) { return kt == 1 ? 256 : (kt == 2 ? 128 : 64); }  // rows per Gram block
 template <int KT>
 struct GramShape {
@@ -362,20 +362,19 @@ __global__ __launch_bounds__(256) void k_lr_gram(const float* __restrict__ ypart
     }
 }
 
-// Threads per tensor of the factorisation (one workgroup per tensor).
+// Threads of a factorisation (every solve workgroup factorises its tensor's Gram).
 constexpr int kCholThreads = 256;
 
+// G = sum of the tensor's block Grams in block order, then the right-looking Cholesky
+// G = L L^T with the rank guard (pivot <= 1e-10 trace(G) -> dead column), in LDS.  The
+// whole workgroup (kCholThreads threads) takes part; L is complete when it returns.
 template <int KT>
-__global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restrict__ gpart, double* __restrict__ lfac,
-                                                  int* __restrict__ alive, int64_t gblocks, int k) {
+__device__ __forceinline__ void chol_factor(const double* __restrict__ gb, int64_t gblocks, int k,
+                                            double (*G)[16 * KT + 1], double (*L)[16 * KT + 1]) {
     constexpr int kp = 16 * KT;
-    __shared__ double G[kp][kp + 1];  // Gram; its lower triangle is updated in place
-    __shared__ double L[kp][kp + 1];  // the factor, written column by column
     const int tid = threadIdx.x;
-    const int64_t b = blockIdx.x;
-    const double* gb = gpart + b * gblocks * kp * kp;
-    // G = sum of the block Grams in block order.  The loads of kBlkBatch blocks are
-    // issued together (indices past the last block re-read it and are not added).
+    // The loads of kBlkBatch blocks are issued together (indices past the last block
+    // re-read it and are not added).
     constexpr int kEPT = (kp * kp + kCholThreads - 1) / kCholThreads;
     constexpr int kBlkBatch = KT == 4 ? 4 : 8;
     double gs[kEPT];
@@ -407,12 +406,12 @@ __global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restri
     for (int j = 0; j < kp; ++j) tr += G[j][j];
     const double thresh = 1e-10 * tr;
     __syncthreads();  // every trace read precedes the in-place factorisation
-    // Right-looking Cholesky with one barrier per column.  Every thread reads the pivot
-    // d = G[j][j].  Column j of L goes to its own array, and the trailing lower
-    // triangle is updated from the unscaled column, G[i][l] -= G[i][j] G[l][j] / d for
-    // j < l <= i: the phase reads column j and writes only columns right of it.
-    // One reciprocal square root per column gives the pivot sqrt(d) = d / sqrt(d), the
-    // column scale 1 / sqrt(d) and 1 / d, which keeps the phase's dependent chain short.
+    // One barrier per column.  Every thread reads the pivot d = G[j][j].  Column j of L
+    // goes to its own array, and the trailing lower triangle is updated from the
+    // unscaled column, G[i][l] -= G[i][j] G[l][j] / d for j < l <= i: the phase reads
+    // column j and writes only columns right of it.  One reciprocal square root per
+    // column gives the pivot sqrt(d) = d / sqrt(d), the column scale 1 / sqrt(d) and
+    // 1 / d, which keeps the phase's dependent chain short.
     static_assert(kp * kp % kCholThreads == 0, "the update covers whole rounds of the workgroup");
     for (int j = 0; j < kp; ++j) {
         const double d = G[j][j];
@@ -428,45 +427,55 @@ __global__ __launch_bounds__(kCholThreads) void k_lr_chol(const double* __restri
         }
         __syncthreads();
     }
-    // Out: L below the diagonal, 1 / L[j][j] on it (0 for a dead column, whose pivot
-    // is 0), zeros above.
-    double* lb = lfac + b * kp * kp;
-    for (int e = tid; e < kp * kp; e += kCholThreads) {
-        const int j = e / kp, i = e % kp;
-        lb[e] = i < j ? L[j][i] : (i == j && L[j][j] > 0.0 ? 1.0 / L[j][j] : 0.0);
-    }
-    if (tid < kp) alive[b * kp + tid] = L[tid][tid] > 0.0 ? 1 : 0;
 }
 
-// P[row] = Y[row] L^-T by forward substitution, p_j = (y_j - sum_{i<j} L[j][i] p_i) /
-// L[j][j], in fp64, one row per thread, in place over Y.  A dead column has 1/L[j][j]
-// = 0 and zeros below it in L, so its p_j is 0 and it feeds nothing later.  The factor
-// is staged in LDS by one cooperative load; every lane then reads the same address
-// (a broadcast).
+// orth's second launch, per tensor and block of 256 rows: the factorisation of the
+// tensor's Gram (chol_factor; each of the tensor's workgroups computes the same L, in
+// the same order, so one launch replaces a per-tensor factorisation and the solve that
+// waited for it), then P[row] = Y[row] L^-T by forward substitution,
+// p_j = (y_j - sum_{i<j} L[j][i] p_i) / L[j][j], in fp64, one row per thread, in place
+// over Y.  A dead column has 1/L[j][j] = 0 and zeros below it in L, so its p_j is 0 and
+// it feeds nothing later; the tensor's first workgroup writes the alive flags.  Every
+// lane reads the same factor address in the substitution (a broadcast).
 // In the last iteration (cmax not null) the workgroup also writes the INT4 quantizer's
 // column maxima of its 256 rows of P = U: cmax[b][block][kk] = max |P[row][kk]| (rows
 // past m count as 0), nblk the blocks of U and V per tensor.
 template <int KT>
-__global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const double* __restrict__ lfac,
+__global__ __launch_bounds__(256) void k_lr_solve(float* __restrict__ p, const double* __restrict__ gpart,
+                                                   int* __restrict__ alive, int64_t gblocks, int k,
                                                    int64_t m, int64_t batch, float* __restrict__ cmax,
                                                    int64_t nblk) {
+    static_assert(kCholThreads == 256, "the factorisation runs on the solve's workgroup");
     constexpr int kp = 16 * KT;
-    __shared__ double lb[kp * kp];
+    __shared__ double G[kp][kp + 1];  // Gram, updated in place; then the substitution's factor
+    __shared__ double L[kp][kp + 1];
     __shared__ float cm[4][kp];
     const int64_t rblocks = (m + 255) / 256;
     const int64_t b = blockIdx.x / rblocks;
     const int64_t blk = blockIdx.x % rblocks;
     const int64_t row = blk * 256 + threadIdx.x;
-    for (int e = threadIdx.x; e < kp * kp; e += 256) lb[e] = lfac[b * kp * kp + e];
-    __syncthreads();
     const bool in = row < m;
+    // this thread's row of Y, loaded before the factorisation so its latency is hidden
+    float* pr = p + (b * m + (in ? row : m - 1)) * kp;
+    vf4 yv[kp / 4];
+#pragma unroll
+    for (int i = 0; i < kp; i += 4) yv[i / 4] = ld4(pr + i);
+    chol_factor<KT>(gpart + b * gblocks * kp * kp, gblocks, k, G, L);
+    // The factor of the substitution: L below the diagonal, 1 / L[j][j] on it (0 for a
+    // dead column, whose pivot is 0), zeros above; G is no longer read.
+    double* lb = &G[0][0];
+    for (int e = threadIdx.x; e < kp * kp; e += 256) {
+        const int j = e / kp, i = e % kp;
+        lb[e] = i < j ? L[j][i] : (i == j && L[j][j] > 0.0 ? 1.0 / L[j][j] : 0.0);
+    }
+    if (blk == 0 && threadIdx.x < kp) alive[b * kp + threadIdx.x] = L[threadIdx.x][threadIdx.x] > 0.0 ? 1 : 0;
+    __syncthreads();
     float pf[kp];
     if (in) {
-        float* pr = p + (b * m + row) * kp;
         double x[kp];
 #pragma unroll
         for (int i = 0; i < kp; i += 4) {
-            const vf4 v = ld4(pr + i);
+            const vf4 v = yv[i / 4];
             x[i] = v[0]; x[i + 1] = v[1]; x[i + 2] = v[2]; x[i + 3] = v[3];
         }
 #pragma unroll
@@ -1301,7 +1310,7 @@ int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 // factorisation, one workgroup per tensor).
 struct LowrankGrids {
     int64_t kp, nseg, fwgs, gblocks;  // fwgs: workgroups (strip ranges) of a fused pass
-    int64_t project_first, project, gram, chol, solve, backproject, backfore, quant, reconstruct;
+    int64_t project_first, project, gram, solve, backproject, backfore, quant, reconstruct;
     bool fused;  // iterations after the first run the fused pass
 };
 
@@ -1313,7 +1322,6 @@ LowrankGrids lowrank_grids(int64_t m, int64_t n, int rank, int64_t batch, bool s
     g.project_first = round8(batch * ((m + proj_rows<true>() - 1) / proj_rows<true>()) * g.nseg);
     g.project = round8(batch * ((m + proj_rows<false>() - 1) / proj_rows<false>()) * g.nseg);
     g.gram = batch * g.gblocks;
-    g.chol = batch;
     g.solve = batch * ((m + 255) / 256);
     g.backproject = round8(batch * ((n + kBackCols - 1) / kBackCols));
     g.fused = g.kp <= 32 && m <= kFusedMaxRows;
@@ -1378,15 +1386,11 @@ hipError_t run_lowrank(const ActT* a, float* ahat, float* err, int64_t m, int64_
         void* gargs[] = {(void*)&ws.ypart, (void*)&ws.p, (void*)&ws.gpart, &m, &nseg, &batch,
                          it > 0 && fused ? (void*)&fwgs : (void*)&none, &strips};
         if ((e = go(&k_lr_gram<KT>, grid.gram, gargs, stream)) != hipSuccess) return e;
-        void* cargs[] = {(void*)&ws.gpart, (void*)&ws.lfac, (void*)&ws.alive, &gblocks, &k};
-        if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_chol<KT>),
-                                 dim3(static_cast<unsigned>(grid.chol)), dim3(kCholThreads), cargs, 0,
-                                 stream)) != hipSuccess)
-            return e;
         // the last iteration's solve and back-projection also leave the quantizer's
         // column maxima of U and V in cmax
         float* cmax = it + 1 == iters ? ws.cmax : nullptr;
-        void* sargs[] = {(void*)&ws.p, (void*)&ws.lfac, &m, &batch, (void*)&cmax, &nblk};
+        void* sargs[] = {(void*)&ws.p, (void*)&ws.gpart, (void*)&ws.alive, &gblocks, &k, &m, &batch,
+                         (void*)&cmax, &nblk};
         if ((e = go(&k_lr_solve<KT>, grid.solve, sargs, stream)) != hipSuccess) return e;
         void* bargs[] = {(void*)&ws.r, (void*)&ws.p, (void*)&ws.qt, &m, &n, &batch, &btotal, (void*)&cmax, &nblk, &mblk};
         if (it + 1 == iters) {  // the last Q, the one that is sent
@@ -1536,9 +1540,8 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
     const int64_t sz_p = up(batch * m * kp * 4);
     const int64_t sz_al = up(batch * kp * 4);
     const int64_t sz_g = up(batch * gblocks * kp * kp * 8);
-    const int64_t sz_x = up(batch * kp * kp * 8);
     const int64_t sz_c = up(batch * ((m + 255) / 256 + (n + 255) / 256) * kp * 4);
-    if (bytes) *bytes = static_cast<size_t>(sz_r + sz_qt + sz_y + sz_p + sz_al + sz_g + sz_x + sz_c);
+    if (bytes) *bytes = static_cast<size_t>(sz_r + sz_qt + sz_y + sz_p + sz_al + sz_g + sz_c);
     LowrankWorkspace ws{};
     ws.shared = shared;
     if (base) {
@@ -1555,8 +1558,6 @@ LowrankWorkspace carve_lowrank_workspace(void* base, int64_t m, int64_t n, int r
         c += sz_al;
         ws.gpart = reinterpret_cast<double*>(c);
         c += sz_g;
-        ws.lfac = reinterpret_cast<double*>(c);
-        c += sz_x;
         ws.cmax = reinterpret_cast<float*>(c);
     }
     return ws;
@@ -1568,7 +1569,7 @@ bool lowrank_launches_fit(int64_t m, int64_t n, int rank, int64_t batch) {
                               g.reconstruct};
     for (int64_t b : blocks)
         if (b * 256 > kMaxDispatchItems) return false;
-    return g.chol * kCholThreads <= kMaxDispatchItems && g.backfore * 64 * kFusedWaves <= kMaxDispatchItems;
+    return g.backfore * 64 * kFusedWaves <= kMaxDispatchItems;
 }
 
 hipError_t launch_lowrank_compress(int a_dtype, const void* a, float* ahat, float* err, int64_t m, int64_t n,

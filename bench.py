@@ -635,7 +635,7 @@ def lowrank_rows(torch, np, cf, gen, dev, wl, steps_d, compressed, rows, step_el
             log(f"{name}: the profiled kernels disagree with the fused-pass rule ({sorted(kt)})")
             rows[name]["fused_rule_mismatch"] = True
         if kt:
-            orth = sum(v for k, v in kt.items() if k in ("k_lr_gram", "k_lr_chol", "k_lr_solve"))
+            orth = sum(v for k, v in kt.items() if k in ("k_lr_gram", "k_lr_solve"))
             rows[name]["orth_us_per_call"] = round(orth, 1)
             rows[name]["orth_us_per_iteration"] = round(orth / iters, 1)
             log(f"{name}: kernels (us per call) {kt}; orth {orth:.1f} us per call")
