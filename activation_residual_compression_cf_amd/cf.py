@@ -309,9 +309,13 @@ class Slab:
                 dt, ab + i * n * esz, hb + i * n * 4, None if eb is None else eb + i * n * 4,
                 c * n, s))
 
-    def compress(self, a: torch.Tensor, per_call: int = 2, stream=None, timer: list | None = None):
+    def compress(self, a: torch.Tensor, per_call: int = 2, stream=None, timer: list | None = None,
+                 streams: list | None = None):
         """Compress one step.  With ``timer`` a list, a pair of timing events recorded on
-        the launch stream just before and after every call is appended to it."""
+        the launch stream just before and after every call is appended to it.  With
+        ``streams`` a list of streams, call i goes to streams[i % len(streams)] instead (the
+        calls touch disjoint tensors, so they may overlap); ordering those streams against
+        the inputs and the later consumers is the caller's."""
         if self.err is None:
             raise RuntimeError("receiver slab has no error buffer")
         if a.numel() != self.count * self.numel:
@@ -323,12 +327,13 @@ class Slab:
         cbytes, ng = n * bits // 8, n // GROUP
         f = lib.cf_compress
         ts = None if timer is None else (torch.cuda.current_stream() if stream is None else stream)
-        for i, c in self._chunks(per_call):
+        rr = [_stream(x) for x in streams] if streams else None
+        for j, (i, c) in enumerate(self._chunks(per_call)):
             if ts is not None:
                 ev0 = torch.cuda.Event(enable_timing=True)
                 ev0.record(ts)
             rc = f(bits, dt, ab + i * n * esz, hb + i * n * 4, eb + i * n * 4, cb + i * cbytes,
-                   sb + i * ng * 4, c * n, s)
+                   sb + i * ng * 4, c * n, s if rr is None else rr[j % len(rr)])
             if rc:
                 raise CFError("cf_compress", rc)
             if ts is not None:

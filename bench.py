@@ -560,6 +560,21 @@ def per_layer_row(torch, cf, dev, wl, steps_d, compressed, row):
     it3 = iter(range(10 ** 9))
     ms = time_calls(torch, lambda: graphs[next(it3) % len(graphs)].replay(), 8)
     row("compress1_flux_per_layer_graph", ms, "compress1")
+    # the same 57 calls alternating over two streams: consecutive layers' calls are
+    # independent, so one call's ramp and drain overlap the next call's streaming
+    pair = [torch.cuda.Stream(), torch.cuda.Stream()]
+    it4 = iter(range(10 ** 9))
+
+    def two_streams():
+        cur = torch.cuda.current_stream()
+        for x in pair:
+            x.wait_stream(cur)
+        s1.compress(steps_d[compressed[next(it4) % len(compressed)]], 2, streams=pair)
+        for x in pair:
+            cur.wait_stream(x)
+
+    ms = time_calls(torch, two_streams, 8)
+    row("compress1_flux_per_layer_2streams", ms, "compress1")
     del graphs, s1
     torch.cuda.empty_cache()
 

@@ -103,3 +103,33 @@ def test_side_stream_call_with_its_own_workspace(cf):
         outs.append([ah.clone(), er.clone(), q.clone(), *[p.clone() for p in pay]])
     for x, y in zip(*outs):
         assert torch.equal(x, y)
+
+
+def test_slab_calls_over_two_streams_match_one_stream(cf):
+    """The per-layer pattern with its calls alternating over two streams (Slab.compress
+    with `streams`): every tensor's Ahat, e, codes and scales equal those of the same
+    calls on one stream, over several steps."""
+    dev = cf.require_device()
+    wl = gen.Workload("slab_streams", 256, 3072, 6, 4, "bf16", True)
+    tr = gen.Trajectory(wl, 23)
+    A = [to_dev(tr.next(), dev) for _ in range(wl.steps)]
+    n = wl.m * wl.n
+    say("Slab.compress, 6 tensors in calls of 2, one stream vs two alternating streams")
+    out = []
+    for two in (False, True):
+        slab = cf.Slab(wl.slots, n, 1, dev)
+        slab.init(A[0].reshape(-1), 2)
+        pair = [torch.cuda.Stream(), torch.cuda.Stream()] if two else None
+        for t in range(1, wl.steps):
+            cur = torch.cuda.current_stream()
+            if pair:
+                for x in pair:
+                    x.wait_stream(cur)
+            slab.compress(A[t].reshape(-1), 2, streams=pair)
+            if pair:
+                for x in pair:
+                    cur.wait_stream(x)
+        torch.cuda.synchronize()
+        out.append([x.cpu() for x in (slab.ahat, slab.err, slab.codes, slab.scales)])
+    for x, y in zip(*out):
+        assert torch.equal(x, y)
