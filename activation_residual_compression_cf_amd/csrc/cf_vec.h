@@ -27,9 +27,9 @@ __device__ __forceinline__ void st_nt(float* p, vf4 v) {
 // policy sc1 nt).  A wave builds the resource from a base address it holds in scalar
 // registers (one that is the same in every lane: a kernel argument plus a block or
 // wave index) and a byte length; each lane passes its byte offset from that base.
-// Stores at or past the length are dropped by the hardware.  Measured on a FLUX step
-// of the 14-byte-per-element sender pattern, these stores run about 1.5% faster than
-// plain non-temporal stores.
+// Stores at or past the length are dropped by the hardware.  Measured on a FLUX step of
+// 114 tensors of 1024 x 3072, against plain non-temporal stores: the 1-bit sender 1%
+// faster, the decode 5%, the low-rank sender 1-1.5%.
 constexpr int kStorePolicy = 1 << 1 /* nt */ | 1 << 4 /* sc1 */;
 // A value that is the same in every lane, moved to scalar registers.
 __device__ __forceinline__ int64_t wave_uniform(int64_t v) {

@@ -575,6 +575,22 @@ def per_layer_row(torch, cf, dev, wl, steps_d, compressed, row):
 
     ms = time_calls(torch, two_streams, 8)
     row("compress1_flux_per_layer_2streams", ms, "compress1")
+    # and that fork and join captured in a HIP graph (two parallel branches) and replayed
+    graphs = []
+    for j in range(4):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            cur = torch.cuda.current_stream()
+            for x in pair:
+                x.wait_stream(cur)
+            s1.compress(steps_d[compressed[j % len(compressed)]], 2, streams=pair)
+            for x in pair:
+                cur.wait_stream(x)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    it5 = iter(range(10 ** 9))
+    ms = time_calls(torch, lambda: graphs[next(it5) % len(graphs)].replay(), 8)
+    row("compress1_flux_per_layer_2streams_graph", ms, "compress1")
     del graphs, s1
     torch.cuda.empty_cache()
 

@@ -139,3 +139,41 @@ def test_lowrank_split_call_graph_matches_eager(cf):
         gx, ex = st["graph"], st["eager"]
         for x, y in zip((gx[0], gx[1], gx[2], *gx[3]), (ex[0], ex[1], ex[2], *ex[3])):
             assert torch.equal(x, y), f"replay {t} differs from the eager run"
+
+
+def test_two_stream_per_layer_graph_matches_eager(cf):
+    """The per-layer calls alternating over two streams, forked from and joined to the
+    capture stream, captured as a graph with two parallel branches: every replay equals
+    the eager one-stream run bit for bit."""
+    dev = cf.require_device()
+    wl = gen.Workload("graph2", 256, 3072, 6, 5, "bf16", True)
+    tr = gen.Trajectory(wl, 13)
+    A = [to_dev(tr.next(), dev) for _ in range(wl.steps)]
+    say("graph capture of the per-layer loop over two streams, 1-bit")
+    eager = cf.Slab(wl.slots, wl.numel, 1, dev)
+    graph = cf.Slab(wl.slots, wl.numel, 1, dev)
+    for s in (eager, graph):
+        s.init(A[0], per_call=2)
+    static_a = torch.empty_like(A[0])
+    side = torch.cuda.Stream()
+    pair = [torch.cuda.Stream(), torch.cuda.Stream()]
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        cur = torch.cuda.current_stream()
+        for x in pair:
+            x.wait_stream(cur)
+        graph.compress(static_a, per_call=2, streams=pair)
+        for x in pair:
+            cur.wait_stream(x)
+    torch.cuda.synchronize()
+    for t in range(1, wl.steps):
+        static_a.copy_(A[t])
+        g.replay()
+        eager.compress(A[t], per_call=2)
+        junk = (A[t].float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        for x, y in ((graph.ahat, eager.ahat), (graph.err, eager.err), (graph.codes, eager.codes),
+                     (graph.scales, eager.scales)):
+            assert torch.equal(x, y), f"replay {t} differs from the eager run"
