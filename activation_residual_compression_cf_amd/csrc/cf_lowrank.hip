@@ -1302,6 +1302,89 @@ __global__ __launch_bounds__(256) void k_lr_reconstruct(const ActT* __restrict__
     }
 }
 
+// Reconstruction with INT4 factors of rank K <= 8 when every row is a whole number of
+// 256-element runs (n % 256 == 0): one-wave blocks over kRvRows rows x 256 columns, in
+// runs per XCD like the element-wise senders, so each load and store instruction is one
+// 1 KiB run of state.  R^[row][col] = sum over kk of U^[row][kk] V^[col][kk] on the
+// vector unit (2 K flops per element, one fused multiply-add per term, kk in order).
+// Lane l dequantizes V^ rows col .. col + 3 (K / 2 dwords of codes) once for the wave's
+// rows; each U^ row is shared by the wave's lanes.  Sender and receiver both take this
+// kernel for such calls, so their results stay identical.
+// Measured on the FLUX batch at rank 8 against the 32-row MFMA kernel (three interleaved
+// runs each): 2 rows per wave, r8/q10 step 3.955 against 3.967 ms and the receiver 0.444
+// against 0.455 ms; 1 row, 3.936 and 0.457 ms (the dequantization per element costs the
+// receiver, whose stream is shorter); 4 rows, 3.966 and 0.448 ms.
+constexpr int kRvRows = 2;  // rows per wave of k_lr_reconstruct_v
+template <bool HAS_E, typename ActT, int K>
+__global__ __launch_bounds__(64) void k_lr_reconstruct_v(const ActT* __restrict__ a, float* __restrict__ ahat,
+                                                          float* __restrict__ err, const void* __restrict__ u,
+                                                          const float* __restrict__ u_scales,
+                                                          const void* __restrict__ v,
+                                                          const float* __restrict__ v_scales, int64_t m,
+                                                          int64_t n, int k, int64_t batch, int64_t total) {
+    static_assert(K % 2 == 0 && K <= 8, "even rank up to 8");
+    constexpr int R = kRvRows;
+    const uint32_t tile = run_order_block<kRunWaves>();
+    if (tile >= total) return;  // total: tiles of R rows x 256 columns in the batch, below 2^31
+    const int lane = threadIdx.x & 63;
+    // the tile's first row of the batch and its column block, in 32-bit arithmetic (uniform)
+    const uint32_t tpr = static_cast<uint32_t>(n >> 8);
+    const uint32_t rgrp = tile / tpr;
+    const uint32_t rg0 = rgrp * R;  // first row of the batch; the R rows lie in one tensor
+    const uint32_t b = rg0 / static_cast<uint32_t>(m);
+    const int64_t c0 = static_cast<int64_t>(tile - rgrp * tpr) * 256;
+    const int64_t col = c0 + 4 * lane;
+    using RA = RawAct<ActT>;
+    typename RA::T xr[R];
+    vf4 h[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        const int64_t off = static_cast<int64_t>(rg0 + q) * n + col;
+        xr[q] = HAS_E ? RA::load(a, off) : RA::zero();
+        h[q] = ld_nt(ahat + off);
+    }
+    const uint8_t* ub = static_cast<const uint8_t*>(u) + static_cast<int64_t>(rg0) * (K / 2);  // U rows of the batch
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(v) +
+                                                           static_cast<int64_t>(b) * (n * K / 2) + col * (K / 2));
+    uint8_t ubyte[R][K / 2];
+    uint32_t w[K / 2];
+#pragma unroll
+    for (int d = 0; d < K / 2; ++d) {
+        w[d] = vw[d];
+#pragma unroll
+        for (int q = 0; q < R; ++q) ubyte[q][d] = ub[q * (K / 2) + d];
+    }
+    auto sext = [](uint32_t c) { return static_cast<float>(static_cast<int>(c ^ 8u) - 8); };
+    // V^[col + c][kk], shared by the R rows
+    float vx[4][K];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk) {
+            const int ni = c * K + kk;  // nibble of V^[col + c][kk] within the lane's dwords
+            vx[c][kk] = sext((w[ni >> 3] >> (4 * (ni & 7))) & 0xFu) * v_scales[b * K + kk];
+        }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        float us[K];
+#pragma unroll
+        for (int kk = 0; kk < K; ++kk)
+            us[kk] = sext((kk & 1) ? (ubyte[q][kk >> 1] >> 4) : (ubyte[q][kk >> 1] & 0xFu)) * u_scales[b * K + kk];
+        vf4 rh;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < K; ++kk) acc = fmaf(us[kk], vx[c][kk], acc);
+            rh[c] = acc;
+        }
+        const vf4 hn = h[q] + rh;
+        const int64_t run = static_cast<int64_t>(rg0 + q) * n + c0;
+        st_stream_run(ahat + run, hn);
+        if constexpr (HAS_E) st_stream_run(err + run, RA::cvt(xr[q]) - hn);
+    }
+}
+
 // ------------------------------------------------------------- launchers --
 int64_t round8(int64_t x) { return (x + 7) & ~int64_t(7); }
 
@@ -1349,8 +1432,33 @@ hipError_t launch_reconstruct_fb(int k, int64_t total, void** args, hipStream_t 
     return go(&k_lr_reconstruct<HAS_E, ActT, FB, 16>, total, args, stream);
 }
 
+// Whether a reconstruction runs on the vector unit (k_lr_reconstruct_v); the sender and
+// the receiver take the same decision.
+bool reconstruct_on_valu(int factor_bits, int k, int64_t m, int64_t n, int64_t batch) {
+    return factor_bits == 4 && k <= 8 && n % 256 == 0 && batch * m * n / 256 < (int64_t(1) << 31);
+}
+
+template <bool HAS_E, typename ActT, int K>
+hipError_t launch_reconstruct_v(void** args, int64_t tiles, hipStream_t stream) {
+    // the last argument, the grid total, is the tile count for this kernel
+    void* vargs[12];
+    for (int i = 0; i < 11; ++i) vargs[i] = args[i];
+    vargs[11] = &tiles;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&k_lr_reconstruct_v<HAS_E, ActT, K>),
+                           dim3(static_cast<unsigned>(tiles)), dim3(64), vargs, 0, stream);
+}
+
 template <bool HAS_E, typename ActT>
 hipError_t launch_reconstruct(int factor_bits, int k, int64_t total, void** args, hipStream_t stream) {
+    const int64_t m = *static_cast<int64_t*>(args[7]), n = *static_cast<int64_t*>(args[8]);
+    const int64_t batch = *static_cast<int64_t*>(args[10]);
+    if (reconstruct_on_valu(factor_bits, k, m, n, batch)) {
+        const int64_t tiles = batch * m / kRvRows * (n / 256);
+        if (k == 2) return launch_reconstruct_v<HAS_E, ActT, 2>(args, tiles, stream);
+        if (k == 4) return launch_reconstruct_v<HAS_E, ActT, 4>(args, tiles, stream);
+        if (k == 6) return launch_reconstruct_v<HAS_E, ActT, 6>(args, tiles, stream);
+        return launch_reconstruct_v<HAS_E, ActT, 8>(args, tiles, stream);
+    }
     if (factor_bits == 4) return launch_reconstruct_fb<HAS_E, ActT, 4>(k, total, args, stream);
     if (factor_bits == 16) return launch_reconstruct_fb<HAS_E, ActT, 16>(k, total, args, stream);
     return launch_reconstruct_fb<HAS_E, ActT, 32>(k, total, args, stream);
