@@ -342,6 +342,35 @@ def test_receiver_matches_sender(cf, dev, fb):
         assert torch.equal(rx, ahat)
 
 
+@pytest.mark.parametrize("rank,n,dtype", [(2, 512, "bf16"), (4, 768, "f32"), (6, 512, "bf16"), (8, 768, "bf16")])
+def test_vector_reconstruction_ranks(cf, dev, O, rank, n, dtype):
+    """INT4 factors of rank <= 8 with n a multiple of 256 take the reconstruction on the
+    vector unit, one instantiation per even rank: each against the oracle from the shared
+    state for 2 steps (3 tensors of 96 rows), err == a - Ahat everywhere, and the
+    receiver identical to the sender."""
+    m = 96
+    wl = gen.Workload("lrv", m, n, 3, 3, dtype, True)
+    say(f"lowrank vector-unit reconstruction: {m}x{n} rank={rank} {dtype}")
+    tr = gen.Trajectory(wl, 6)
+    A0 = tr.next()
+    a0 = to_dev(A0, dev)
+    ahat = torch.empty((3, m, n), dtype=torch.float32, device=dev)
+    err = torch.empty_like(ahat)
+    cf.init_state(a0, ahat, err)
+    rx = torch.empty_like(ahat)
+    cf.init_state(a0, rx)
+    qs = torch.from_numpy(start_bases(6, 3, n, rank)).to(dev)
+    prev = A0
+    for t in range(1, 3):
+        A = tr.next()
+        payload = check_step(cf, dev, O, prev, A, ahat, err, qs, rank, 2, 4, samples=[0, 1, 2],
+                             tol=1e-3, cold=t == 1)
+        cf.lowrank_decompress(4, payload, rx, rank)
+        torch.cuda.synchronize()
+        assert torch.equal(rx, ahat), f"step {t}: receiver differs from sender"
+        prev = A
+
+
 @pytest.mark.parametrize("rank,iters", [(32, 2), (8, 10)])
 def test_flux_shape(cf, dev, O, rank, iters):
     """114 x (1024 x 3072) bf16 per call, INT4 factors; two compressed steps; oracle on

@@ -62,7 +62,7 @@ def test_topk_without_err(cf, offset):
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("rank,iters,fb", [(32, 2, 4), (8, 2, 16)])
+@pytest.mark.parametrize("rank,iters,fb", [(32, 2, 4), (8, 2, 16), (8, 2, 4)])
 def test_lowrank_without_err(cf, rank, iters, fb):
     dev = cf.require_device()
     wl = gen.Workload("noerrl", 512, 3072, 3, 3, "bf16", True)
