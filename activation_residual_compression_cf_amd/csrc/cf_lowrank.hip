@@ -37,6 +37,8 @@
 //   k_lr_reconstruct Ahat += U^ V^^T (MFMA, factors dequantized on the fly from the
 //                   payload) and e = a - Ahat; the receiver runs the same kernel
 //                   without e, so both sides produce identical bits.
+//   k_lr_reconstruct_v the same on the vector unit for INT4 factors of rank <= 8 when n
+//                   is a multiple of 256 (sender and receiver alike).
 // Every reduction has a fixed order; there are no atomics.
 
 #include "cf_internal.h"
